@@ -1,0 +1,168 @@
+"""CPU oracle for single-query softmax attention (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package. It never touches the GPU library and shares no code with it.
+
+Two independent evaluations of the same definition live here:
+
+* ``aaren_oracle.c`` -- the constant-memory recurrence of the "Self-attention
+  Does Not Need O(n^2) Memory" review (section 2 Algorithm), stabilised by a
+  running maximum, in float64 with OpenMP over independent units. It is fast
+  enough for every workload at full size.
+* ``brute.py`` -- the definition written out (softmax of all prefix scores,
+  then the weighted sum), O(N^2 d), plus the combine operator used to check
+  that any bracketing of the scan gives the same result.
+
+The functions below take numpy arrays (float32 inputs; bfloat16 inputs must be
+widened to float32 by the caller, which is exact) and return float64 arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "aaren_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc (-O2, OpenMP). Returns its path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                        "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _configure(lib):
+    """Declare the argument and result types of a loaded oracle library."""
+    f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+    f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+    i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
+    opt64 = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_scan.argtypes = [f32p, f32p, f32p, i64, i64, i64, i64, ctypes.c_double,
+                                f64p, opt64, opt64]
+    lib.oracle_scan_segmented.argtypes = [f32p, f32p, f32p, i64p, i64, i64, i64, i64,
+                                          ctypes.c_double, f64p, opt64, opt64]
+    lib.oracle_step.argtypes = [f32p, f32p, f32p, f64p, f64p, f64p, opt64,
+                                i64, i64, i64, ctypes.c_double]
+    lib.oracle_reduce.argtypes = [f32p, f32p, f32p, i64, i64, i64, i64, ctypes.c_double,
+                                  f64p, opt64, opt64]
+    for fn in (lib.oracle_scan, lib.oracle_scan_segmented, lib.oracle_step, lib.oracle_reduce):
+        fn.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = _configure(ctypes.CDLL(build()))
+    return _lib
+
+
+def _f32(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != np.float32:
+        raise TypeError(f"oracle inputs are float32 (got {a.dtype}); widen bfloat16 first")
+    return np.ascontiguousarray(a)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs with."""
+    return int(_load().oracle_threads())
+
+
+def scan(q, k, v, scale, stats: bool = False):
+    """Many-to-many output. q [H,d], k,v [B,H,N,d] float32 -> o [B,H,N,d] float64
+    (and, with stats, the running max m and L = m + ln u, both [B,H,N])."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, N, d = k.shape
+    assert q.shape == (H, d) and v.shape == k.shape
+    o = np.empty((B, H, N, d), np.float64)
+    m = np.empty((B, H, N), np.float64) if stats else None
+    lse = np.empty((B, H, N), np.float64) if stats else None
+    rc = _load().oracle_scan(q, k, v, B, H, N, d, float(scale), o, _ptr(m), _ptr(lse))
+    if rc:
+        raise ValueError("oracle_scan rejected its arguments")
+    return (o, m, lse) if stats else o
+
+
+def scan_segmented(q, k, v, offsets, scale, stats: bool = False):
+    """Each packed sequence scanned on its own. q [H,d], k,v [T,H,d] float32,
+    offsets int64 [S+1] -> o [T,H,d] float64 (and m, L [T,H] with stats)."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    offsets = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    T, H, d = k.shape
+    S = offsets.size - 1
+    o = np.empty((T, H, d), np.float64)
+    m = np.empty((T, H), np.float64) if stats else None
+    lse = np.empty((T, H), np.float64) if stats else None
+    rc = _load().oracle_scan_segmented(q, k, v, offsets, S, T, H, d, float(scale), o,
+                                       _ptr(m), _ptr(lse))
+    if rc:
+        raise ValueError("oracle_scan_segmented rejected its arguments")
+    return (o, m, lse) if stats else o
+
+
+def state_init(S, H, d):
+    """A fresh (empty) state: m = -inf, u = 0, w = 0."""
+    return (np.full((S, H), -np.inf), np.zeros((S, H)), np.zeros((S, H, d)))
+
+
+def step(q, k_t, v_t, state, scale):
+    """Absorb one pair per (stream, head) into state = (m, u, w) (float64,
+    updated in place) and return o_t [S,H,d] float64."""
+    q, k_t, v_t = _f32(q), _f32(k_t), _f32(v_t)
+    S, H, d = k_t.shape
+    m, u, w = state
+    for a in (m, u, w):
+        assert a.dtype == np.float64 and a.flags.c_contiguous
+    o = np.empty((S, H, d), np.float64)
+    rc = _load().oracle_step(q, k_t, v_t, m, u, w, _ptr(o), S, H, d, float(scale))
+    if rc:
+        raise ValueError("oracle_step rejected its arguments")
+    return o
+
+
+def reduce(q, k, v, scale, stats: bool = False):
+    """Many-to-one output. q [H,d], k,v [B,H,N,d] -> o [B,H,d] float64
+    (and m, L [B,H] with stats)."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, N, d = k.shape
+    o = np.empty((B, H, d), np.float64)
+    m = np.empty((B, H), np.float64) if stats else None
+    lse = np.empty((B, H), np.float64) if stats else None
+    rc = _load().oracle_reduce(q, k, v, B, H, N, d, float(scale), o, _ptr(m), _ptr(lse))
+    if rc:
+        raise ValueError("oracle_reduce rejected its arguments")
+    return (o, m, lse) if stats else o
+
+
+def max_scaled_err(got, ref) -> float:
+    """max over elements of |got - ref| / (1 + |ref|): the error measure the
+    tolerances are stated in. NaN where either side is NaN counts as failure
+    unless both are NaN."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise ValueError(f"shape mismatch {got.shape} vs {ref.shape}")
+    if got.size == 0:
+        return 0.0
+    both_nan = np.isnan(got) & np.isnan(ref)
+    err = np.abs(got - ref) / (1.0 + np.abs(ref))
+    err = np.where(both_nan, 0.0, err)
+    if np.isnan(err).any():
+        return float("inf")
+    return float(err.max())

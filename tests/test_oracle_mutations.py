@@ -1,0 +1,106 @@
+"""Plant a plausible mistake in a copy of the oracle and require the pins to
+catch it (no GPU). Each mutant is compiled into a temporary directory; the
+real oracle is never modified."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import _pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "aaren_oracle.c")
+
+# (name, function the edit is confined to or None for the whole file, old, new)
+MUTATIONS = [
+    ("rescale exponent sign flipped", None, "exp(*m - s)", "exp(s - *m)"),
+    ("normaliser not rescaled", None, "*u = *u * shrink + 1.0;", "*u = *u + 1.0;"),
+    ("value sum not rescaled", None, "w[j] = w[j] * shrink + (double)v[j];",
+     "w[j] = w[j] + (double)v[j];"),
+    ("no max subtraction", None, "double p = exp(s - *m);", "double p = exp(s);"),
+    ("running max starts at 0, not -inf", "oracle_scan", "double m = -INFINITY, u = 0.0;",
+     "double m = 0.0, u = 0.0;"),
+    ("running max never raised", None, "*m = s;", ";"),
+    ("new-maximum term weighted by e^s", None, "*u = *u * shrink + 1.0;",
+     "*u = *u * shrink + exp(s);"),
+    ("key index wrong", None, "(double)q[j] * (double)k[j]", "(double)q[j] * (double)k[0]"),
+    ("scale dropped", None, "return scale * acc;", "return acc;"),
+    ("scale applied twice", None, "return scale * acc;", "return scale * scale * acc;"),
+    ("no final division", None, "o[j] = w[j] / u;", "o[j] = w[j];"),
+    ("log-normaliser without max", None, "*lse_out = m + log(u);", "*lse_out = log(u);"),
+    ("exclusive instead of inclusive output", "oracle_scan",
+     "absorb(&m, &u, w, d, score(qh, k + row * d, d, scale), v + row * d);\n"
+     "                emit(m, u, w, d, o + row * d, m_out ? m_out + row : NULL,\n"
+     "                     lse_out ? lse_out + row : NULL);",
+     "if (i == 0) { for (int64_t j = 0; j < d; ++j) o[row * d + j] = 0.0; }\n"
+     "                else emit(m, u, w, d, o + row * d, m_out ? m_out + row : NULL,\n"
+     "                     lse_out ? lse_out + row : NULL);\n"
+     "                absorb(&m, &u, w, d, score(qh, k + row * d, d, scale), v + row * d);"),
+    ("segmented: query of head 0 for all heads", "oracle_scan_segmented",
+     "score(q + h * d, k + row * d", "score(q, k + row * d"),
+    ("segmented: head stride dropped", "oracle_scan_segmented",
+     "int64_t row = t * H + h;", "int64_t row = t * H + (h > 0 ? h - 1 : 0);"),
+    ("segmented: state not restarted per sequence", "oracle_scan_segmented",
+     "for (int64_t t = offsets[seq]; t < offsets[seq + 1]; ++t) {",
+     "for (int64_t t = (seq > 0 ? offsets[seq - 1] : 0); t < offsets[seq + 1]; ++t) {"),
+    ("step: key and value swapped", "oracle_step", "score(qh, k_t + unit * d",
+     "score(qh, v_t + unit * d"),
+    ("step: query of the wrong head", "oracle_step", "const float *qh = q + (unit % H) * d;",
+     "const float *qh = q + (unit / H % H) * d;"),
+    ("reduce drops the last pair", "oracle_reduce", "for (int64_t i = 0; i < N; ++i)",
+     "for (int64_t i = 0; i < N - 1; ++i)"),
+    ("reduce reads rows of the wrong unit", "oracle_reduce", "int64_t row = unit * N + i;",
+     "int64_t row = (unit % H) * N + i;"),
+]
+
+
+def _mutate(src, func, old, new):
+    if func is None:
+        assert old in src, old
+        return src.replace(old, new)
+    start = src.index("int " + func + "(")
+    nxt = src.find("\nint ", start + 1)
+    end = len(src) if nxt < 0 else nxt
+    body = src[start:end]
+    assert old in body, (func, old)
+    return src[:start] + body.replace(old, new) + src[end:]
+
+
+class _Bound:
+    """The oracle module's functions, bound to another build of the library."""
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def __getattr__(self, name):
+        fn = getattr(oracle, name)
+        if not callable(fn):
+            return fn
+
+        def call(*a, **kw):
+            saved = oracle._lib
+            oracle._lib = self._lib
+            try:
+                return fn(*a, **kw)
+            finally:
+                oracle._lib = saved
+        return call
+
+
+@pytest.mark.parametrize("name,func,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(tmp_path, name, func, old, new):
+    src = open(SRC).read()
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(_mutate(src, func, old, new))
+    lib_path = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-w",
+                    "-o", str(lib_path), str(mutant), "-lm"], check=True)
+    bound = _Bound(oracle._configure(ctypes.CDLL(str(lib_path))))
+    caught = []
+    for check in _pins.ALL:
+        try:
+            check(bound)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(check.__name__)
+    assert caught, f"no pin catches the planted mistake '{name}'"
