@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of libaaren on one MI355X, against the HBM roofline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the hot path over one batch of the workload, inputs
+already resident in HBM:
+  dense, single, long_bf16 : one aaren_scan call          (token-heads = B*H*N)
+  ragged                   : one aaren_scan_segmented call (token-heads = H*T)
+  stream                   : aaren_state_init + 256 aaren_step calls
+                                                           (token-heads = S*H*256)
+  reduce                   : one aaren_reduce call         (keys = B*H*N)
+W untimed steps, then exactly K steps between two HIP events recorded on the
+stream the kernels run on. Prints one JSON line. The default workload is the
+dense batch (B=32, H=8, N=4096, d=64, fp32) the headline metric is quoted on.
+
+roofline.achieved = algorithmic bytes per launch of the dominant kernel /
+its average duration over the timed region; algorithmic bytes = K and V read
+once and O written once (plus the state for the step). roofline.traffic is the
+HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled
+by the same counters on a plain copy of known size), read from the committed
+counter file under profiles/ only while the kernel sources still hash to the
+value recorded there; otherwise null.
+
+cpu_baseline times the float64 CPU oracle (as it is, untuned) on the host's
+cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+KERNEL_SOURCES = {
+    "scan": ["scan.hip", "device.h", "layout.h"],
+    "step": ["step.hip", "device.h", "layout.h"],
+    "reduce": ["reduce.hip", "device.h", "layout.h"],
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "exact_softmax_attention_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter file, or None
+    if there is none or the kernel changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}.counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_sha256") != source_hash(kind):
+        return None
+    return (c["fetch_kib_per_dispatch"] * 1024 * c["copy_fetch_factor"] +
+            c["write_kib_per_dispatch"] * 1024 * c["copy_write_factor"])
+
+
+class Workload:
+    """A prepared workload: step() runs one pass; the numbers describe it."""
+    kind = "scan"
+    unit = "token-heads/s"
+    launches_per_step = 1
+
+
+def make(name: str, device):
+    import numpy as np
+    import torch
+
+    import exact_softmax_attention_02_amd as aaren
+    import workloads as wl
+
+    w = wl.WORKLOADS[name]
+    z = w.sizes
+    b = Workload()
+    b.name, b.describe = name, w.describe()
+    b.dtype = {"f32": "f32", "bf16": "bf16->f32"}[w.dtype]
+
+    if w.kind == "dense":
+        B, H, N, d = z["B"], z["H"], z["N"], z["d"]
+        q, k, v = wl.dense_inputs(B, H, N, d, w.seed, device=device, dtype=w.dtype,
+                                  score_span=w.score_span)
+        scale = wl.default_scale(d)
+        o = torch.empty(B, H, N, d, device=device)
+        ws = torch.zeros(aaren.aaren_scan_workspace_size(B, H, N, d), dtype=torch.uint8,
+                         device=device)
+        b.step = lambda: aaren.aaren_scan(q, k, v, scale, out=o, workspace=ws)
+        b.units = B * H * N
+        b.bytes_per_launch = 2 * k.numel() * k.element_size() + o.numel() * 4
+        b.config = {"workload": f"dense many-to-many scan {b.describe}", "B": B, "H": H, "N": N,
+                    "d": d, "in_dtype": w.dtype, "out_dtype": "f32"}
+        b.kernel = "scan_kernel"
+
+        def cpu(budget_s):
+            import oracle
+            qh, kh, vh = (t.float().cpu().numpy() for t in (q, k, v))
+            rows = B if name != "long_bf16" else 1      # long_bf16: one batch row
+            kh, vh = kh[:rows], vh[:rows]
+            done, t0 = 0, time.perf_counter()
+            while True:
+                oracle.scan(qh, kh, vh, scale)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return (done * rows * H * N / dt,
+                    f"{done} pass(es) over {rows}x{H}x{N} (d={d}) of the workload's inputs")
+        b.cpu = cpu
+
+    elif w.kind == "segmented":
+        H, d = z["H"], z["d"]
+        lengths = wl.segment_lengths(z["num_seqs"], z["max_len"], w.seed)
+        q, k, v, offs = wl.segmented_inputs(lengths, H, d, w.seed, device=device)
+        T = int(lengths.sum())
+        scale = wl.default_scale(d)
+        o = torch.empty(T, H, d, device=device)
+        ws = torch.zeros(aaren.aaren_scan_segmented_workspace_size(len(lengths), T, H, d),
+                         dtype=torch.uint8, device=device)
+        b.step = lambda: aaren.aaren_scan_segmented(q, k, v, offs, scale, out=o, workspace=ws)
+        b.units = H * T
+        b.bytes_per_launch = 3 * T * H * d * 4 + offs.numel() * 8
+        b.config = {"workload": f"packed ragged many-to-many scan {b.describe}",
+                    "num_seqs": len(lengths), "total_tokens": T, "H": H, "d": d,
+                    "in_dtype": "f32", "out_dtype": "f32"}
+        b.kernel = "scan_kernel (segmented)"
+
+        def cpu(budget_s):
+            import oracle
+            ho = offs.cpu().numpy()
+            qh = q.cpu().numpy()
+            n = 1
+            while n < len(lengths) and ho[n] < 2_000_000:
+                n += 1
+            kh, vh = k[:ho[n]].cpu().numpy(), v[:ho[n]].cpu().numpy()
+            done, t0 = 0, time.perf_counter()
+            while True:
+                oracle.scan_segmented(qh, kh, vh, ho[:n + 1], scale)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return done * H * int(ho[n]) / dt, (f"{done} pass(es) over the first {n} sequences "
+                                                 f"({int(ho[n])} tokens x {H} heads)")
+        b.cpu = cpu
+
+    elif w.kind == "step":
+        S, H, d, T = z["S"], z["H"], z["d"], z["steps"]
+        q, k, v = wl.step_inputs(S, H, d, T, w.seed, device=device)
+        scale = wl.default_scale(d)
+        m, u, st_w = aaren.new_state(S, H, d, device=device)
+        o = torch.empty(S, H, d, device=device)
+
+        def step():
+            aaren.aaren_state_init(m, u, st_w)
+            for t in range(T):
+                aaren.aaren_step(q, k[t], v[t], m, u, st_w, scale, o_t=o)
+        b.step = step
+        b.kind = "step"
+        b.units = S * H * T
+        b.launches_per_step = T
+        b.bytes_per_launch = S * H * (4 * d * 4 + 4 * 4)  # k,v,w read + w,o written; m,u r/w
+        b.config = {"workload": f"RNN step, {T} appends per stream {b.describe}", "S": S, "H": H,
+                    "d": d, "appends": T, "in_dtype": "f32", "out_dtype": "f32"}
+        b.kernel = "step_kernel"
+
+        def cpu(budget_s):
+            import oracle
+            ns = 4096
+            qh, kh, vh = q.cpu().numpy(), k[:, :ns].cpu().numpy(), v[:, :ns].cpu().numpy()
+            done, t0 = 0, time.perf_counter()
+            while True:
+                st = oracle.state_init(ns, H, d)
+                for t in range(T):
+                    oracle.step(qh, kh[t], vh[t], st, scale)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return done * ns * H * T / dt, f"{done} pass(es) over {ns} streams x {H} heads x {T} appends"
+        b.cpu = cpu
+
+    else:  # reduce
+        B, H, N, d = z["B"], z["H"], z["N"], z["d"]
+        q, k, v = wl.reduce_inputs(B, H, N, d, w.seed, device=device)
+        scale = wl.default_scale(d)
+        o = torch.empty(B, H, d, device=device)
+        ws = torch.empty(aaren.aaren_reduce_workspace_size(B, H, N, d), dtype=torch.uint8,
+                         device=device)
+        b.step = lambda: aaren.aaren_reduce(q, k, v, scale, out=o, workspace=ws)
+        b.kind = "reduce"
+        b.unit = "keys/s"
+        b.units = B * H * N
+        b.bytes_per_launch = 2 * k.numel() * 4 + o.numel() * 4
+        b.config = {"workload": f"many-to-one reduction {b.describe}", "B": B, "H": H, "N": N,
+                    "d": d, "in_dtype": "f32", "out_dtype": "f32"}
+        b.kernel = "reduce_partial_kernel + reduce_final_kernel"
+
+        def cpu(budget_s):
+            import oracle
+            qh, kh, vh = q.cpu().numpy(), k.cpu().numpy(), v.cpu().numpy()
+            done, t0 = 0, time.perf_counter()
+            while True:
+                oracle.reduce(qh, kh, vh, scale)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return done * B * H * N / dt, f"{done} pass(es) over all {N} keys (one unit: 1 thread)"
+        b.cpu = cpu
+    return b
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense",
+                    choices=["single", "dense", "long_bf16", "ragged", "stream", "reduce"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU-oracle time budget for cpu_baseline (0 to skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path is data-parallel over independent "
+              "sequences and this build runs on a single MI355X; --gpus must be 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    device = torch.device("cuda:0")
+    b = make(args.workload, device)
+    stream = torch.cuda.current_stream(device)
+    for _ in range(args.warmup):
+        b.step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        b.step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    value = b.units / (ms / 1e3)
+    launch_s = ms / 1e3 / b.launches_per_step
+    achieved = b.bytes_per_launch / launch_s / 1e9
+    traffic = measured_traffic(b.kind, args.workload)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        rate, sample = b.cpu(args.cpu_seconds)
+        cores = oracle.threads() if args.workload != "reduce" else 1
+        cpu = {"value": rate, "unit": b.unit, "cores": cores, "kind": "oracle", "sample": sample}
+
+    line = {
+        "metric": "tokens/s and achieved HBM GB/s (% of peak) for aaren_scan at B*H*N, d=64/128"
+                  if b.kind == "scan" else f"{b.unit} for {args.workload}",
+        "value": value,
+        "unit": b.unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.dtype,
+        "data": "synthetic (seeded i.i.d. normal inputs; no dataset)",
+        "config": b.config,
+        "achieved_GBps": achieved,
+        "peak_frac": achieved / PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": b.kernel, "algorithmic_bytes_per_launch": b.bytes_per_launch},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

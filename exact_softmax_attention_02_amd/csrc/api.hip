@@ -1,0 +1,449 @@
+// C ABI of libaaren: argument validation, workspace sizing and dispatch.
+// Every check runs before anything is enqueued, so a non-OK status leaves the
+// outputs untouched. The kernels live in scan.hip, step.hip and reduce.hip.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+
+#include "layout.h"
+
+#define AAREN_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+aaren_status fail(aaren_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char *e = std::getenv("AAREN_LOG");
+        return e && e[0] && e[0] != '0';
+    }();
+    return on;
+}
+
+bool aligned16(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+bool dtype_ok(aaren_dtype t)
+{
+    return t == AAREN_F32 || t == AAREN_BF16;
+}
+
+size_t dtype_bytes(aaren_dtype t)
+{
+    return t == AAREN_F32 ? 4 : 2;
+}
+
+// a*b*... without overflow past 2^62, else -1
+int64_t mul_checked(std::initializer_list<int64_t> xs)
+{
+    int64_t r = 1;
+    for (int64_t x : xs) {
+        if (x < 0)
+            return -1;
+        if (x != 0 && r > (int64_t(1) << 62) / x)
+            return -1;
+        r *= x;
+    }
+    return r;
+}
+
+aaren_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess)
+        return AAREN_OK;
+    return fail(AAREN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+aaren_status check_common(int64_t d, aaren_dtype in, aaren_dtype out)
+{
+    if (d != 64 && d != 128)
+        return fail(AAREN_ERR_UNSUPPORTED, "d = %lld: supported head dimensions are 64 and 128",
+                    (long long)d);
+    if (!dtype_ok(in) || !dtype_ok(out))
+        return fail(AAREN_ERR_UNSUPPORTED, "unknown dtype (in %d, out %d)", (int)in, (int)out);
+    return AAREN_OK;
+}
+
+aaren_status check_ptr(const void *p, const char *name)
+{
+    if (!p)
+        return fail(AAREN_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned16(p))
+        return fail(AAREN_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+    return AAREN_OK;
+}
+
+#define CHECK(expr)                          \
+    do {                                     \
+        aaren_status st_ = (expr);           \
+        if (st_ != AAREN_OK)                 \
+            return st_;                      \
+    } while (0)
+
+size_t scan_workspace_bytes(int64_t tiles, int64_t bitmap_words, int64_t d)
+{
+    return aaren::kHeaderBytes + aaren::round256((size_t)bitmap_words * 4) +
+           (size_t)tiles * 2 * aaren::slot_words((int)d) * 8;
+}
+
+int64_t ceil_div(int64_t a, int64_t b)
+{
+    return (a + b - 1) / b;
+}
+
+}  // namespace
+
+AAREN_API int aaren_version(void)
+{
+    return 100;  // 0.1.0
+}
+
+AAREN_API const char *aaren_status_string(aaren_status s)
+{
+    switch (s) {
+    case AAREN_OK: return "ok";
+    case AAREN_ERR_INVALID_ARG: return "invalid argument";
+    case AAREN_ERR_UNSUPPORTED: return "unsupported";
+    case AAREN_ERR_ALIGNMENT: return "misaligned pointer";
+    case AAREN_ERR_WORKSPACE: return "workspace too small";
+    case AAREN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+AAREN_API const char *aaren_last_error(void)
+{
+    return g_last_error;
+}
+
+AAREN_API aaren_status aaren_workspace_clear(void *workspace, size_t workspace_bytes,
+                                             void *hip_stream)
+{
+    if (workspace_bytes == 0)
+        return AAREN_OK;
+    CHECK(check_ptr(workspace, "workspace"));
+    return hip_status(aaren::launch_fill_zero(workspace, workspace_bytes,
+                                              static_cast<hipStream_t>(hip_stream)),
+                      "workspace clear launch");
+}
+
+// ---- dense scan ---------------------------------------------------------------
+
+AAREN_API size_t aaren_scan_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d)
+{
+    if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128))
+        return 0;
+    const int64_t tiles = mul_checked({B, H, ceil_div(N, aaren::scan_tile_rows_min((int)d))});
+    if (tiles < 0)
+        return 0;
+    return scan_workspace_bytes(tiles, 0, d);
+}
+
+AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, int64_t B,
+                                  int64_t H, int64_t N, int64_t d, float scale,
+                                  aaren_dtype in_dtype, aaren_dtype out_dtype, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream)
+{
+    if (B < 0 || H < 0 || N < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
+                    (long long)B, (long long)H, (long long)N);
+    CHECK(check_common(d, in_dtype, out_dtype));
+    const int64_t elems = mul_checked({B, H, N, d});
+    if (elems < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "B*H*N*d overflows");
+    if (elems == 0)
+        return AAREN_OK;
+    CHECK(check_ptr(q, "q"));
+    CHECK(check_ptr(k, "k"));
+    CHECK(check_ptr(v, "v"));
+    CHECK(check_ptr(o, "o"));
+    const int rows = aaren::scan_rows_per_tile((int)d, in_dtype);
+    const int64_t chunks = ceil_div(N, rows);
+    const int64_t tiles = B * H * chunks;
+    if (tiles >= 0x7fffffff)
+        return fail(AAREN_ERR_UNSUPPORTED, "%lld tiles exceed the 2^31-1 launch limit",
+                    (long long)tiles);
+    const size_t need = scan_workspace_bytes(tiles, 0, d);
+    if (!workspace || workspace_bytes < need)
+        return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    need);
+    if (!aligned16(workspace))
+        return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+
+    aaren::ScanParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.bitmap = nullptr;
+    p.bitmap_words = 0;
+    p.rows = N;
+    p.streams = B * H;
+    p.H = H;
+    p.stream_stride = N * d;
+    p.row_stride = d;
+    p.chunks = chunks;
+    p.num_tiles = (uint32_t)tiles;
+    p.qscale = scale * 1.44269504088896340736f;
+    p.header = static_cast<uint32_t *>(workspace);
+    p.slots = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(workspace) + aaren::kHeaderBytes);
+    if (log_enabled())
+        fprintf(stderr, "[aaren] scan B=%lld H=%lld N=%lld d=%lld tiles=%lld rows/tile=%d\n",
+                (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles, rows);
+    return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, false,
+                                         static_cast<hipStream_t>(hip_stream)),
+                      "scan launch");
+}
+
+// ---- segmented scan -------------------------------------------------------------
+
+AAREN_API size_t aaren_scan_segmented_workspace_size(int64_t num_seqs, int64_t total_tokens,
+                                                     int64_t H, int64_t d)
+{
+    if (num_seqs < 0 || total_tokens < 0 || H < 0 || (d != 64 && d != 128))
+        return 0;
+    const int64_t tiles = mul_checked({H, ceil_div(total_tokens, aaren::scan_tile_rows_min((int)d))});
+    if (tiles < 0)
+        return 0;
+    return scan_workspace_bytes(tiles, ceil_div(total_tokens, 32), d);
+}
+
+AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const void *v, void *o,
+                                            const int64_t *offsets, int64_t num_seqs,
+                                            int64_t total_tokens, int64_t H, int64_t d,
+                                            float scale, aaren_dtype in_dtype,
+                                            aaren_dtype out_dtype, void *workspace,
+                                            size_t workspace_bytes, void *hip_stream)
+{
+    if (num_seqs < 0 || total_tokens < 0 || H < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (num_seqs %lld, T %lld, H %lld)",
+                    (long long)num_seqs, (long long)total_tokens, (long long)H);
+    CHECK(check_common(d, in_dtype, out_dtype));
+    if (num_seqs == 0 && total_tokens != 0)
+        return fail(AAREN_ERR_INVALID_ARG, "no sequences but %lld tokens", (long long)total_tokens);
+    const int64_t elems = mul_checked({total_tokens, H, d});
+    if (elems < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "T*H*d overflows");
+    if (elems == 0)
+        return AAREN_OK;
+    if (!offsets)
+        return fail(AAREN_ERR_INVALID_ARG, "offsets is NULL");
+    if ((reinterpret_cast<uintptr_t>(offsets) & 7u) != 0)
+        return fail(AAREN_ERR_ALIGNMENT, "offsets is not 8-byte aligned");
+    CHECK(check_ptr(q, "q"));
+    CHECK(check_ptr(k, "k"));
+    CHECK(check_ptr(v, "v"));
+    CHECK(check_ptr(o, "o"));
+    const int rows = aaren::scan_rows_per_tile((int)d, in_dtype);
+    const int64_t chunks = ceil_div(total_tokens, rows);
+    const int64_t tiles = H * chunks;
+    if (tiles >= 0x7fffffff)
+        return fail(AAREN_ERR_UNSUPPORTED, "%lld tiles exceed the 2^31-1 launch limit",
+                    (long long)tiles);
+    const int64_t words = ceil_div(total_tokens, 32);
+    const size_t need = scan_workspace_bytes(tiles, words, d);
+    if (!workspace || workspace_bytes < need)
+        return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    need);
+    if (!aligned16(workspace))
+        return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint32_t *bitmap = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes);
+    aaren::ScanParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.bitmap = bitmap;
+    p.bitmap_words = words;
+    p.rows = total_tokens;
+    p.streams = H;
+    p.H = H;
+    p.stream_stride = d;
+    p.row_stride = H * d;
+    p.chunks = chunks;
+    p.num_tiles = (uint32_t)tiles;
+    p.qscale = scale * 1.44269504088896340736f;
+    p.header = static_cast<uint32_t *>(workspace);
+    p.slots = reinterpret_cast<uint64_t *>(ws + aaren::kHeaderBytes +
+                                           aaren::round256((size_t)words * 4));
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (log_enabled())
+        fprintf(stderr, "[aaren] scan_segmented S=%lld T=%lld H=%lld d=%lld tiles=%lld\n",
+                (long long)num_seqs, (long long)total_tokens, (long long)H, (long long)d,
+                (long long)tiles);
+    CHECK(hip_status(aaren::launch_segment_flags(offsets, num_seqs, total_tokens, bitmap, words, st),
+                     "segment flag launch"));
+    return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, true, st),
+                      "segmented scan launch");
+}
+
+// ---- RNN step -----------------------------------------------------------------
+
+AAREN_API aaren_status aaren_state_init(float *m, float *u, float *w, int64_t S, int64_t H,
+                                        int64_t d, void *hip_stream)
+{
+    if (S < 0 || H < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (S %lld, H %lld)", (long long)S,
+                    (long long)H);
+    if (d != 64 && d != 128)
+        return fail(AAREN_ERR_UNSUPPORTED, "d = %lld: supported head dimensions are 64 and 128",
+                    (long long)d);
+    const int64_t units = mul_checked({S, H, d});
+    if (units < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "S*H*d overflows");
+    if (units == 0)
+        return AAREN_OK;
+    if (!m || !u || !w)
+        return fail(AAREN_ERR_INVALID_ARG, "state pointer is NULL");
+    if (!aligned16(w))
+        return fail(AAREN_ERR_ALIGNMENT, "w is not 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(u)) & 3u)
+        return fail(AAREN_ERR_ALIGNMENT, "m or u is not 4-byte aligned");
+    return hip_status(aaren::launch_state_init(m, u, w, S * H, d,
+                                               static_cast<hipStream_t>(hip_stream)),
+                      "state init launch");
+}
+
+AAREN_API aaren_status aaren_step(const void *q, const void *k_t, const void *v_t, float *m,
+                                  float *u, float *w, void *o_t, int64_t S, int64_t H, int64_t d,
+                                  float scale, aaren_dtype in_dtype, aaren_dtype out_dtype,
+                                  void *hip_stream)
+{
+    if (S < 0 || H < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (S %lld, H %lld)", (long long)S,
+                    (long long)H);
+    CHECK(check_common(d, in_dtype, out_dtype));
+    const int64_t elems = mul_checked({S, H, d});
+    if (elems < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "S*H*d overflows");
+    if (elems == 0)
+        return AAREN_OK;
+    CHECK(check_ptr(q, "q"));
+    CHECK(check_ptr(k_t, "k_t"));
+    CHECK(check_ptr(v_t, "v_t"));
+    CHECK(check_ptr(w, "w"));
+    if (o_t)
+        CHECK(check_ptr(o_t, "o_t"));
+    if (!m || !u)
+        return fail(AAREN_ERR_INVALID_ARG, "m or u is NULL");
+    if ((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(u)) & 3u)
+        return fail(AAREN_ERR_ALIGNMENT, "m or u is not 4-byte aligned");
+    aaren::StepParams p{};
+    p.q = q;
+    p.k = k_t;
+    p.v = v_t;
+    p.m = m;
+    p.u = u;
+    p.w = w;
+    p.o = o_t;
+    p.units = S * H;
+    p.H = H;
+    p.scale = scale;
+    return hip_status(aaren::launch_step(p, (int)d, in_dtype, out_dtype,
+                                         static_cast<hipStream_t>(hip_stream)),
+                      "step launch");
+}
+
+// ---- many-to-one reduction ------------------------------------------------------
+
+namespace {
+
+// chunks per (b,h): enough workgroups to cover the chip a few times, at least
+// one iteration of rows each, at most kReduceMaxParts
+int64_t reduce_parts(int64_t units, int64_t N, int64_t d)
+{
+    const int64_t per_iter = aaren::reduce_rows_per_iteration((int)d, AAREN_F32) <
+                                     aaren::reduce_rows_per_iteration((int)d, AAREN_BF16)
+                                 ? aaren::reduce_rows_per_iteration((int)d, AAREN_F32)
+                                 : aaren::reduce_rows_per_iteration((int)d, AAREN_BF16);
+    int64_t parts = ceil_div(2048, units > 0 ? units : 1);
+    const int64_t by_rows = ceil_div(N, per_iter);
+    if (parts > by_rows)
+        parts = by_rows;
+    if (parts > aaren::kReduceMaxParts)
+        parts = aaren::kReduceMaxParts;
+    return parts < 1 ? 1 : parts;
+}
+
+}  // namespace
+
+AAREN_API size_t aaren_reduce_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d)
+{
+    if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128))
+        return 0;
+    const int64_t units = mul_checked({B, H});
+    if (units < 0)
+        return 0;
+    const int64_t n = mul_checked({units, reduce_parts(units, N, d), aaren::slot_words((int)d), 4});
+    return n < 0 ? 0 : (size_t)n;
+}
+
+AAREN_API aaren_status aaren_reduce(const void *q, const void *k, const void *v, void *o,
+                                    float *m_out, float *u_out, int64_t B, int64_t H, int64_t N,
+                                    int64_t d, float scale, aaren_dtype in_dtype,
+                                    aaren_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                                    void *hip_stream)
+{
+    if (B < 0 || H < 0 || N < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
+                    (long long)B, (long long)H, (long long)N);
+    CHECK(check_common(d, in_dtype, out_dtype));
+    const int64_t units = mul_checked({B, H});
+    if (units < 0 || mul_checked({B, H, N, d}) < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "B*H*N*d overflows");
+    if (units == 0)
+        return AAREN_OK;
+    if (N == 0)
+        return fail(AAREN_ERR_INVALID_ARG, "N = 0: attention over no pairs has no value");
+    if (units > 0x7fffffff / aaren::kReduceMaxParts)
+        return fail(AAREN_ERR_UNSUPPORTED, "B*H = %lld is too large", (long long)units);
+    CHECK(check_ptr(q, "q"));
+    CHECK(check_ptr(k, "k"));
+    CHECK(check_ptr(v, "v"));
+    CHECK(check_ptr(o, "o"));
+    if ((reinterpret_cast<uintptr_t>(m_out) | reinterpret_cast<uintptr_t>(u_out)) & 3u)
+        return fail(AAREN_ERR_ALIGNMENT, "m_out or u_out is not 4-byte aligned");
+    const int64_t parts = reduce_parts(units, N, d);
+    const size_t need = (size_t)units * parts * aaren::slot_words((int)d) * 4;
+    if (!workspace || workspace_bytes < need)
+        return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    need);
+    if (!aligned16(workspace))
+        return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+    aaren::ReduceParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.m_out = m_out;
+    p.u_out = u_out;
+    p.partials = static_cast<float *>(workspace);
+    p.units = units;
+    p.H = H;
+    p.N = N;
+    p.parts = parts;
+    p.rows_per_part = ceil_div(N, parts);
+    p.qscale = scale * 1.44269504088896340736f;
+    if (log_enabled())
+        fprintf(stderr, "[aaren] reduce B=%lld H=%lld N=%lld d=%lld parts=%lld rows/part=%lld\n",
+                (long long)B, (long long)H, (long long)N, (long long)d, (long long)parts,
+                (long long)p.rows_per_part);
+    return hip_status(aaren::launch_reduce(p, (int)d, in_dtype, out_dtype,
+                                           static_cast<hipStream_t>(hip_stream)),
+                      "reduce launch");
+}

@@ -1,0 +1,173 @@
+// Device helpers for the libaaren kernels (gfx950, wave64).
+//
+// Row geometry: a key/value row of D elements is read 16 bytes per lane, so a
+// row is spread over kLanes consecutive lanes of one wavefront ("a group") and
+// one wave-wide load covers kGroupsPerWave rows. Every row the workloads use
+// is 256 bytes (d=64 fp32 or d=128 bf16): 16 lanes x 16 B, 4 rows per wave.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace aaren {
+
+// Storage type of a bfloat16 element (raw bits).
+struct bf16 {
+    uint16_t bits;
+};
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegInf = -__builtin_inff();
+
+template <int D, typename Tin>
+struct RowGeo {
+    static constexpr int kElems = 16 / (int)sizeof(Tin);  // elements per lane load
+    static constexpr int kLanes = D / kElems;             // lanes sharing one row
+    static constexpr int kGroupsPerWave = 64 / kLanes;    // rows per wave-wide load
+    static_assert(kLanes >= 4 && kLanes <= 32 && (kLanes & (kLanes - 1)) == 0,
+                  "a row must span 4..32 lanes");
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 load16(const void *p)
+{
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ void store16(void *p, u32x4 v)
+{
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// Widen one 16-byte chunk into E floats (bf16 -> fp32 is exact).
+template <typename T>
+__device__ __forceinline__ void widen(u32x4 raw, float *out);
+
+template <>
+__device__ __forceinline__ void widen<float>(u32x4 raw, float *out)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        out[i] = __uint_as_float(raw[i]);
+}
+
+template <>
+__device__ __forceinline__ void widen<bf16>(u32x4 raw, float *out)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(raw[i] << 16);
+        out[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+    }
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t bf16_bits(float f)
+{
+    uint32_t x = __float_as_uint(f);
+    if ((x & 0x7fffffffu) > 0x7f800000u)
+        return (x >> 16) | 0x40u;
+    return (x + 0x7fffu + ((x >> 16) & 1u)) >> 16;
+}
+
+// Store E consecutive floats of a row as Tout (E = 4 or 8).
+template <typename Tout, int E>
+__device__ __forceinline__ void store_row(Tout *dst, const float *x)
+{
+    if constexpr (sizeof(Tout) == 4) {
+#pragma unroll
+        for (int c = 0; c < E / 4; ++c) {
+            u32x4 v = {__float_as_uint(x[4 * c]), __float_as_uint(x[4 * c + 1]),
+                       __float_as_uint(x[4 * c + 2]), __float_as_uint(x[4 * c + 3])};
+            store16(reinterpret_cast<float *>(dst) + 4 * c, v);
+        }
+    } else {
+        uint32_t w[E / 2];
+#pragma unroll
+        for (int i = 0; i < E / 2; ++i)
+            w[i] = bf16_bits(x[2 * i]) | (bf16_bits(x[2 * i + 1]) << 16);
+        if constexpr (E == 8) {
+            u32x4 v = {w[0], w[1], w[2], w[3]};
+            store16(dst, v);
+        } else {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            u32x2 v = {w[0], w[1]};
+            *reinterpret_cast<u32x2 *>(dst) = v;
+        }
+    }
+}
+
+// Load E consecutive floats of q (any Tin) from a 16-byte aligned row offset.
+template <typename Tin, int E>
+__device__ __forceinline__ void load_query(const Tin *q, float *out)
+{
+    widen<Tin>(load16(q), out);
+}
+
+// x + (x from the lane selected by the DPP control); the whole wave is active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x)
+{
+    return x + __builtin_bit_cast(
+                   float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF,
+                                                      0xF, true));
+}
+
+// Sum over the L lanes of a group (L = 4, 8, 16 or 32, aligned): a butterfly,
+// so every lane ends with the bitwise-identical sum.
+template <int L>
+__device__ __forceinline__ float group_sum(float x)
+{
+    x = dpp_add<0xB1>(x);  // quad_perm [1,0,3,2]: lane ^ 1
+    x = dpp_add<0x4E>(x);  // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (L >= 8)
+        x = dpp_add<0x141>(x);  // row_half_mirror: the other quad of 8 lanes
+    if constexpr (L >= 16)
+        x = dpp_add<0x140>(x);  // row_mirror: the other half of 16 lanes
+    if constexpr (L >= 32)
+        x += __builtin_bit_cast(float,
+                                __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+    return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x)
+{
+    return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float rcp_fast(float x)
+{
+    return __builtin_amdgcn_rcpf(x);
+}
+
+// Weights for combining two states with maxima ma and mb (log2 units):
+// m = max(ma, mb), fa = 2^(ma - m), fb = 2^(mb - m). An empty side (-inf)
+// gets weight 0; two empty sides give m = -inf, fa = 1, fb = 0.
+__device__ __forceinline__ void merge_weights(float ma, float mb, float &m, float &fa, float &fb)
+{
+    const bool b_big = mb > ma;
+    const float hi = b_big ? mb : ma;
+    const float lo = b_big ? ma : mb;
+    float e = exp2_fast(lo - hi);
+    e = (lo == kNegInf) ? 0.f : e;
+    fa = b_big ? e : 1.f;
+    fb = b_big ? 1.f : e;
+    m = hi;
+}
+
+// 64-bit agent-scope relaxed accesses (coherent across the XCDs' L2s).
+__device__ __forceinline__ void st_agent(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace aaren

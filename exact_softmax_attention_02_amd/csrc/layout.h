@@ -1,0 +1,126 @@
+// Workspace layout, tile shapes and kernel parameters of libaaren (host and
+// device). Nothing here is part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "aaren.h"
+
+namespace aaren {
+
+// ---- scan workspace ---------------------------------------------------------
+// [ header: 64 x u32 ][ segment-start bitmap (segmented scan only) ][ tile slots ]
+// header[kEpoch]  : epoch of the last completed call (0 after clearing)
+// header[kTicket] : next tile ticket of the running call (0 between calls)
+// header[kDone]   : tiles finished by the running call (0 between calls)
+// header[kError]  : set (never cleared by a call) when a tile gave up waiting
+//                   for its predecessors or found the counters inconsistent --
+//                   only possible with a workspace that was not zero-filled
+//                   before first use or was shared by overlapping calls
+// Tile slots: per tile two published states ("aggregate" then "inclusive
+// prefix"), each kSlotWords(D) 64-bit words: word 0 = m, word 1 = u, words
+// 2.. = w[0..D-1]. A word is (tag << 32) | float bits, tag = epoch << 1 | flag,
+// so a reader can tell a word of the running call from a stale one without
+// any fence; flag marks an aggregate that contains a sequence start.
+constexpr int kEpoch = 0;
+constexpr int kTicket = 1;
+constexpr int kDone = 2;
+constexpr int kError = 3;
+// polls of a predecessor's slots before a tile gives up (about a second)
+constexpr uint32_t kMaxPolls = 1u << 20;
+constexpr size_t kHeaderBytes = 256;
+
+__host__ __device__ constexpr int slot_words(int D)
+{
+    return ((D + 2) + 7) / 8 * 8;
+}
+
+__host__ __device__ constexpr size_t round256(size_t b)
+{
+    return (b + 255) / 256 * 256;
+}
+
+// Rows one scan tile covers, per (d, input dtype). Row = 256 B for d=64 fp32
+// and d=128 bf16; each of the 16 lane groups of a 4-wave tile owns 16 rows.
+__host__ __device__ constexpr int scan_tile_rows(int D, int in_bytes)
+{
+    // lanes per row = D*in_bytes/16, groups per tile = 4 waves * 64 / lanes
+    return (4 * 64 / (D * in_bytes / 16)) * 16;
+}
+
+// Smallest tile over the supported input dtypes (sizes the workspace query).
+__host__ __device__ constexpr int scan_tile_rows_min(int D)
+{
+    return scan_tile_rows(D, 4) < scan_tile_rows(D, 2) ? scan_tile_rows(D, 4)
+                                                       : scan_tile_rows(D, 2);
+}
+
+struct ScanParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    const uint32_t *bitmap;  // segment starts, one bit per row (segmented only)
+    int64_t bitmap_words;
+    int64_t rows;            // rows per stream: N (dense) or T (segmented)
+    int64_t streams;         // B*H (dense) or H (segmented)
+    int64_t H;
+    int64_t stream_stride;   // elements between stream bases: N*d or d
+    int64_t row_stride;      // elements between rows of a stream: d or H*d
+    int64_t chunks;          // tiles per stream
+    uint32_t num_tiles;
+    float qscale;            // scale * log2(e)
+    uint32_t *header;
+    uint64_t *slots;
+};
+
+struct StepParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    float *m;
+    float *u;
+    float *w;
+    void *o;
+    int64_t units;  // S*H
+    int64_t H;
+    float scale;
+};
+
+struct ReduceParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    float *m_out;
+    float *u_out;
+    float *partials;      // [units][parts][slot_words(d)] floats: m, u, w[d]
+    int64_t units;        // B*H
+    int64_t H;
+    int64_t N;
+    int64_t parts;        // chunks per unit
+    int64_t rows_per_part;
+    float qscale;         // scale * log2(e)
+};
+
+constexpr int kReduceMaxParts = 1024;
+
+// Launchers (each validates nothing: the API layer did).
+hipError_t launch_scan(const ScanParams &p, int D, aaren_dtype in, aaren_dtype out, bool segmented,
+                       hipStream_t stream);
+hipError_t launch_segment_flags(const int64_t *offsets, int64_t num_seqs, int64_t total_tokens,
+                                uint32_t *bitmap, int64_t words, hipStream_t stream);
+int scan_rows_per_tile(int D, aaren_dtype in);
+hipError_t launch_step(const StepParams &p, int D, aaren_dtype in, aaren_dtype out,
+                       hipStream_t stream);
+hipError_t launch_state_init(float *m, float *u, float *w, int64_t units, int64_t D,
+                             hipStream_t stream);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
+hipError_t launch_reduce(const ReduceParams &p, int D, aaren_dtype in, aaren_dtype out,
+                         hipStream_t stream);
+int reduce_rows_per_iteration(int D, aaren_dtype in);
+
+}  // namespace aaren

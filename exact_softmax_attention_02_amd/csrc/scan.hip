@@ -1,0 +1,497 @@
+// Many-to-many single-query attention as one streaming prefix scan.
+//
+// What is computed ("Attention as an RNN" review, abstract item (3) and
+// proposed method; the recurrence is that of section 2 of the
+// "Self-attention Does Not Need O(n^2) Memory" review): for every prefix
+// 1..k of a sequence, o_k = sum_{i<=k} e^{s_i} v_i / sum_{i<=k} e^{s_i} with
+// s_i = scale <q, k_i>. The prefix is carried as a state (m, u, w) -- running
+// maximum, normaliser and weighted value sum relative to e^m -- and two states
+// combine associatively: (m_a,u_a,w_a) (+) (m_b,u_b,w_b) = (m, f_a u_a + f_b u_b,
+// f_a w_a + f_b w_b), m = max(m_a, m_b), f = e^{m_side - m}.
+//
+// Design (one HBM pass over K and V, one over O):
+//  * A tile is ROWS consecutive rows of one stream (a (b,h) sequence, or one
+//    head of a packed batch). A lane group of L lanes reads one 16-byte slice
+//    of R consecutive rows per lane, so every wave-wide load is four (or
+//    more) fully used 256-byte row segments.
+//  * Scores: per-lane partial dot products, summed over the group with a DPP
+//    butterfly (no MFMA: the score is a matrix-vector product, bandwidth-bound).
+//  * Pass 1 reduces each group's rows to one state (maximum first, then the
+//    sums, so no chained rescaling); the groups' states go through LDS.
+//  * Cross-tile carry by decoupled look-back: a tile publishes its aggregate
+//    state at once, then walks back over predecessor tiles of its stream until
+//    one has published an inclusive prefix, and publishes its own. Tiles take
+//    tickets in launch order from a counter, so a tile only ever waits for
+//    tiles that already run. Published words carry an epoch tag, so readers
+//    need no fence and the workspace never has to be reset between calls.
+//  * Pass 2 re-runs each group's rows from its exclusive prefix with a running
+//    maximum (outputs need the per-row maximum: a shared tile maximum would
+//    underflow early rows when scores span more than ~87), normalises and
+//    stores.
+//  * Packed batches: a bitmap marks sequence starts; a start resets the state,
+//    and the look-back stops at an aggregate that holds a start (segmented
+//    scan with head flags).
+// Exponentials are base 2: q is pre-multiplied by scale*log2(e).
+#include "device.h"
+
+namespace aaren {
+
+template <int D, typename Tin, int R, int WAVES>
+struct ScanShape {
+    using G = RowGeo<D, Tin>;
+    static constexpr int E = G::kElems;
+    static constexpr int L = G::kLanes;
+    static constexpr int GPW = G::kGroupsPerWave;
+    static constexpr int NG = WAVES * GPW;  // lane groups per tile
+    static constexpr int ROWS = NG * R;     // rows per tile
+    static constexpr int SLOT = slot_words(D);
+    static constexpr int CPL = D / 64;      // columns per lane, column-per-lane layout
+    static_assert(R <= 32, "row flags are kept in 32 bits");
+    static_assert(D % 64 == 0, "d = 64 or 128");
+};
+
+__device__ __forceinline__ uint32_t next_epoch(uint32_t prev)
+{
+    uint32_t e = prev + 1;
+    return (e >= 0x7fffffffu) ? 1u : e;
+}
+
+__device__ __forceinline__ bool tag_ok(uint64_t word, uint32_t epoch)
+{
+    return (uint32_t)(word >> 33) == epoch;
+}
+
+__device__ __forceinline__ float word_value(uint64_t word)
+{
+    return __uint_as_float((uint32_t)word);
+}
+
+// Publish a state in column-per-lane layout (lane j holds w[j + 64c]).
+template <int D>
+__device__ __forceinline__ void publish(uint64_t *slot, uint32_t tag, float m, float u,
+                                        const float *w, int lane)
+{
+    const uint64_t hi = (uint64_t)tag << 32;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c)
+        st_agent(slot + 2 + lane + 64 * c, hi | __float_as_uint(w[c]));
+    if (lane == 0)
+        st_agent(slot + 0, hi | __float_as_uint(m));
+    if (lane == 1)
+        st_agent(slot + 1, hi | __float_as_uint(u));
+}
+
+template <int D, typename Tin, typename Tout, int R, int WAVES, bool SEG>
+__global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
+{
+    using S = ScanShape<D, Tin, R, WAVES>;
+    constexpr int E = S::E, L = S::L, GPW = S::GPW, NG = S::NG, ROWS = S::ROWS;
+    constexpr int SLOT = S::SLOT, CPL = S::CPL;
+
+    __shared__ uint32_t sh_ticket, sh_epoch;
+    __shared__ float sh_gm[NG], sh_gu[NG];
+    __shared__ uint32_t sh_gf[NG];
+    __shared__ __attribute__((aligned(16))) float sh_gw[NG][D];
+    __shared__ float sh_cm, sh_cu;
+    __shared__ __attribute__((aligned(16))) float sh_cw[D];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int gl = lane % L;                     // lane within its group
+    const int grp = wave * GPW + lane / L;       // group within the tile
+
+    if (tid == 0) {
+        sh_ticket = __hip_atomic_fetch_add(p.header + kTicket, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+        sh_epoch = next_epoch(__hip_atomic_load(p.header + kEpoch, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT));
+    }
+    __syncthreads();
+    const uint32_t ticket = __builtin_amdgcn_readfirstlane(sh_ticket);
+    const uint32_t epoch = __builtin_amdgcn_readfirstlane(sh_epoch);
+    if (ticket >= p.num_tiles) {  // counters were not left at zero: refuse to run
+        if (tid == 0)
+            __hip_atomic_fetch_or(p.header + kError, 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const int64_t chunk = ticket / p.streams;
+    const int64_t stream = ticket - chunk * p.streams;
+    const int64_t row0 = chunk * ROWS + (int64_t)grp * R;   // first row of this group
+    const int64_t left = p.rows - row0;
+    const int nvalid = left <= 0 ? 0 : (left >= R ? R : (int)left);
+
+    // ---- issue every load of the group's rows first --------------------------
+    const int64_t base = stream * p.stream_stride + row0 * p.row_stride + gl * E;
+    const Tin *kp = static_cast<const Tin *>(p.k) + base;
+    const Tin *vp = static_cast<const Tin *>(p.v) + base;
+    u32x4 kr[R], vr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        kr[r] = u32x4{0, 0, 0, 0};
+        vr[r] = u32x4{0, 0, 0, 0};
+        if (r < nvalid) {
+            kr[r] = load16(kp + r * p.row_stride);
+            vr[r] = load16(vp + r * p.row_stride);
+        }
+    }
+
+    uint32_t flags = 0;  // bit r: row r of this group starts a sequence
+    if constexpr (SEG) {
+        if (nvalid > 0) {
+            const int64_t wi = row0 >> 5;
+            const int sh = (int)(row0 & 31);
+            uint64_t bits = p.bitmap[wi];
+            if (wi + 1 < p.bitmap_words)
+                bits |= (uint64_t)p.bitmap[wi + 1] << 32;
+            flags = (uint32_t)(bits >> sh);
+            if (nvalid < 32)
+                flags &= (1u << nvalid) - 1u;
+            if constexpr (R < 32)
+                flags &= (1u << R) - 1u;
+        }
+    }
+
+    float qv[E];
+    load_query<Tin, E>(static_cast<const Tin *>(p.q) + (stream % p.H) * D + gl * E, qv);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        qv[e] *= p.qscale;
+
+    // ---- scores (log2 units) ---------------------------------------------------
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float kf[E];
+        widen<Tin>(kr[r], kf);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            part = __builtin_fmaf(qv[e], kf[e], part);
+        s[r] = group_sum<L>(part);
+        s[r] = (r < nvalid) ? s[r] : kNegInf;
+    }
+
+    // ---- pass 1: the group's state (from its last sequence start, if any) ------
+    const int first = (SEG && flags) ? 31 - __builtin_clz(flags) : 0;
+    float gm = kNegInf;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        gm = (r >= first) ? fmaxf(gm, s[r]) : gm;
+    float gu = 0.f, gwv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        gwv[e] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const bool use = (r >= first) && (r < nvalid);
+        const float pr = use ? exp2_fast(s[r] - gm) : 0.f;
+        float vf[E];
+        widen<Tin>(vr[r], vf);
+        gu += pr;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            gwv[e] = __builtin_fmaf(pr, vf[e], gwv[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        sh_gw[grp][gl * E + e] = gwv[e];
+    if (gl == 0) {
+        sh_gm[grp] = gm;
+        sh_gu[grp] = gu;
+        sh_gf[grp] = flags != 0;
+    }
+    __syncthreads();
+
+    // ---- exclusive prefix of the groups before this one (segment-aware) --------
+    auto group_prefix = [&](float &xm, float &xu, float *xw, bool &xf) {
+        xm = kNegInf;
+        xu = 0.f;
+        xf = false;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            xw[e] = 0.f;
+        for (int g = 0; g < grp; ++g) {
+            const float bm = sh_gm[g], bu = sh_gu[g];
+            const bool bf = sh_gf[g] != 0;
+            float m, fa, fb;
+            merge_weights(xm, bm, m, fa, fb);
+            fa = bf ? 0.f : fa;  // a sequence start in g cuts what came before
+            fb = bf ? 1.f : fb;
+            m = bf ? bm : m;
+            xu = fa * xu + fb * bu;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                xw[e] = fa * xw[e] + fb * sh_gw[g][gl * E + e];
+            xm = m;
+            xf = xf || bf;
+        }
+    };
+
+    float pm, pu, pw[E];
+    bool pf;
+    if (wave != 0)
+        group_prefix(pm, pu, pw, pf);
+
+    if (wave == 0) {
+        // tile aggregate, column-per-lane
+        float am = kNegInf, au = 0.f, aw[CPL];
+        bool af = false;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            aw[c] = 0.f;
+        for (int g = 0; g < NG; ++g) {
+            const float bm = sh_gm[g], bu = sh_gu[g];
+            const bool bf = sh_gf[g] != 0;
+            float m, fa, fb;
+            merge_weights(am, bm, m, fa, fb);
+            fa = bf ? 0.f : fa;
+            fb = bf ? 1.f : fb;
+            m = bf ? bm : m;
+            au = fa * au + fb * bu;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                aw[c] = fa * aw[c] + fb * sh_gw[g][lane + 64 * c];
+            am = m;
+            af = af || bf;
+        }
+
+        uint64_t *my = p.slots + (size_t)ticket * 2 * SLOT;
+        float cm = kNegInf, cu = 0.f, cw[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            cw[c] = 0.f;
+        // The carry is needed unless this is the stream's first tile or the
+        // tile's first row starts a sequence (group 0 is lanes 0..L-1 of wave 0).
+        bool first_row_starts = false;
+        if constexpr (SEG)
+            first_row_starts = __builtin_amdgcn_readfirstlane(flags) & 1u;
+        const bool need_carry = chunk > 0 && !first_row_starts;
+        if (need_carry) {
+            if (!af)
+                publish<D>(my, epoch << 1, am, au, aw, lane);
+            else
+                publish<D>(my, (epoch << 1) | 1u, am, au, aw, lane);
+            int64_t pred = (int64_t)ticket - p.streams;
+            uint32_t polls = 0;
+            while (true) {
+                const uint64_t *agg = p.slots + (size_t)pred * 2 * SLOT;
+                const uint64_t *pre = agg + SLOT;
+                uint64_t wp[CPL], wa[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    wp[c] = ld_agent(pre + 2 + lane + 64 * c);
+                    wa[c] = ld_agent(agg + 2 + lane + 64 * c);
+                }
+                const uint64_t pmw = ld_agent(pre + 0), puw = ld_agent(pre + 1);
+                const uint64_t amw = ld_agent(agg + 0), auw = ld_agent(agg + 1);
+                bool pre_ok = tag_ok(pmw, epoch) && tag_ok(puw, epoch);
+                bool agg_ok = tag_ok(amw, epoch) && tag_ok(auw, epoch);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    pre_ok = pre_ok && tag_ok(wp[c], epoch);
+                    agg_ok = agg_ok && tag_ok(wa[c], epoch);
+                }
+                pre_ok = __all(pre_ok);
+                agg_ok = __all(agg_ok);
+                if (pre_ok || agg_ok) {
+                    const float bm = word_value(pre_ok ? pmw : amw);
+                    const float bu = word_value(pre_ok ? puw : auw);
+                    float m, fx, fc;  // the earlier tile goes on the left
+                    merge_weights(bm, cm, m, fx, fc);
+                    cu = fx * bu + fc * cu;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c)
+                        cw[c] = fx * word_value(pre_ok ? wp[c] : wa[c]) + fc * cw[c];
+                    cm = m;
+                    const bool stop = pre_ok || (SEG && ((amw >> 32) & 1u));
+                    if (stop)
+                        break;
+                    if (pred < p.streams) {  // a first tile never publishes an aggregate
+                        if (lane == 0)
+                            __hip_atomic_fetch_or(p.header + kError, 2u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    pred -= p.streams;
+                    continue;
+                }
+                if (++polls > kMaxPolls) {  // bounded wait: give up rather than hang
+                    if (lane == 0)
+                        __hip_atomic_fetch_or(p.header + kError, 4u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        // inclusive prefix = carry (+) aggregate, unless the tile holds a start
+        float im = am, iu = au, iw[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            iw[c] = aw[c];
+        if (!af) {
+            float m, fa, fb;
+            merge_weights(cm, am, m, fa, fb);
+            iu = fa * cu + fb * au;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                iw[c] = fa * cw[c] + fb * aw[c];
+            im = m;
+        }
+        publish<D>(my + SLOT, epoch << 1, im, iu, iw, lane);
+
+        if (lane == 0) {
+            sh_cm = cm;
+            sh_cu = cu;
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            sh_cw[lane + 64 * c] = cw[c];
+        group_prefix(pm, pu, pw, pf);
+    }
+    __syncthreads();
+
+    // ---- pass 2: running state from carry (+) group prefix, normalise, store ---
+    float xm = pm, xu = pu, xw[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        xw[e] = pw[e];
+    if (!pf) {
+        const float cm = sh_cm, cu = sh_cu;
+        float m, fa, fb;
+        merge_weights(cm, pm, m, fa, fb);
+        xu = fa * cu + fb * pu;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            xw[e] = fa * sh_cw[gl * E + e] + fb * pw[e];
+        xm = m;
+    }
+
+    Tout *op = static_cast<Tout *>(p.o) + base;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r < nvalid) {
+            if constexpr (SEG) {
+                if ((flags >> r) & 1u) {
+                    xm = kNegInf;
+                    xu = 0.f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        xw[e] = 0.f;
+                }
+            }
+            const float sr = s[r];
+            const bool up = sr > xm;
+            const float hi = up ? sr : xm;
+            const float lo = up ? xm : sr;
+            const float ex = exp2_fast(lo - hi);
+            const float a = up ? ex : 1.f;
+            const float pr = up ? 1.f : ex;
+            float vf[E];
+            widen<Tin>(vr[r], vf);
+            xu = __builtin_fmaf(xu, a, pr);
+            const float inv = rcp_fast(xu);
+            float ov[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                xw[e] = __builtin_fmaf(xw[e], a, pr * vf[e]);
+                ov[e] = xw[e] * inv;
+            }
+            xm = hi;
+            store_row<Tout, E>(op + r * p.row_stride, ov);
+        }
+    }
+
+    // ---- the last tile of the call leaves the counters ready for the next -----
+    if (tid == 0) {
+        const uint32_t n = __hip_atomic_fetch_add(p.header + kDone, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        if (n == p.num_tiles - 1) {
+            __hip_atomic_store(p.header + kTicket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.header + kDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.header + kEpoch, epoch, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// One thread per 32-row bitmap word: bit b of word i is set when row 32i+b is
+// the first row of a non-empty sequence.
+__global__ __launch_bounds__(256) void segment_flags_kernel(const int64_t *offsets, int64_t S,
+                                                            int64_t T, uint32_t *bitmap,
+                                                            int64_t words)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= words)
+        return;
+    const int64_t lo_row = i * 32;
+    const int64_t hi_row = lo_row + 32 < T ? lo_row + 32 : T;
+    int64_t lo = 0, hi = S;  // first s with offsets[s] >= lo_row
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (offsets[mid] < lo_row)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    uint32_t bits = 0;
+    for (int64_t s = lo; s < S; ++s) {
+        const int64_t o = offsets[s];
+        if (o >= hi_row)
+            break;
+        if (o >= lo_row)
+            bits |= 1u << (uint32_t)(o - lo_row);
+    }
+    bitmap[i] = bits;
+}
+
+template <int D, typename Tin, typename Tout, bool SEG>
+static hipError_t launch_one(const ScanParams &p, hipStream_t stream)
+{
+    constexpr int R = 16, WAVES = 4;
+    static_assert(ScanShape<D, Tin, R, WAVES>::ROWS == scan_tile_rows(D, sizeof(Tin)),
+                  "tile rows disagree with the workspace sizing");
+    hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, SEG>), dim3(p.num_tiles),
+                       dim3(64 * WAVES), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, bool SEG>
+static hipError_t dispatch_dtypes(const ScanParams &p, aaren_dtype in, aaren_dtype out,
+                                  hipStream_t stream)
+{
+    if (in == AAREN_F32 && out == AAREN_F32)
+        return launch_one<D, float, float, SEG>(p, stream);
+    if (in == AAREN_F32 && out == AAREN_BF16)
+        return launch_one<D, float, bf16, SEG>(p, stream);
+    if (in == AAREN_BF16 && out == AAREN_F32)
+        return launch_one<D, bf16, float, SEG>(p, stream);
+    return launch_one<D, bf16, bf16, SEG>(p, stream);
+}
+
+hipError_t launch_scan(const ScanParams &p, int D, aaren_dtype in, aaren_dtype out, bool segmented,
+                       hipStream_t stream)
+{
+    if (D == 64)
+        return segmented ? dispatch_dtypes<64, true>(p, in, out, stream)
+                         : dispatch_dtypes<64, false>(p, in, out, stream);
+    return segmented ? dispatch_dtypes<128, true>(p, in, out, stream)
+                     : dispatch_dtypes<128, false>(p, in, out, stream);
+}
+
+int scan_rows_per_tile(int D, aaren_dtype in)
+{
+    return scan_tile_rows(D, in == AAREN_F32 ? 4 : 2);
+}
+
+hipError_t launch_segment_flags(const int64_t *offsets, int64_t num_seqs, int64_t total_tokens,
+                                uint32_t *bitmap, int64_t words, hipStream_t stream)
+{
+    const int64_t blocks = (words + 255) / 256;
+    hipLaunchKernelGGL(segment_flags_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, offsets,
+                       num_seqs, total_tokens, bitmap, words);
+    return hipGetLastError();
+}
+
+}  // namespace aaren

@@ -1,0 +1,153 @@
+// Constant-memory RNN step: absorb one key/value pair per (stream, head) into
+// a stored state (m, u, w) and emit o_t = w/u ("Attention as an RNN" review,
+// abstract item (4)(ii) and proposed method; the update is the recurrence of
+// section 2 of the "Self-attention Does Not Need O(n^2) Memory" review with
+// the running-maximum shift of its section 3).
+//
+// Pure streaming: each (stream, head) is one lane group that reads q, k_t, v_t,
+// w (16-byte slices) and m, u, and writes w, m, u and o_t. The state stays in
+// natural score units (m is the running maximum of the fp32 scores).
+#include "device.h"
+
+namespace aaren {
+
+template <int D, typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void step_kernel(const StepParams p)
+{
+    using G = RowGeo<D, Tin>;
+    constexpr int E = G::kElems, L = G::kLanes;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t unit = gid / L;
+    const int gl = threadIdx.x % L;
+    if (unit >= p.units)  // whole groups leave together: L divides 256
+        return;
+    const int64_t h = unit % p.H;
+
+    float qv[E], kf[E], vf[E], wv[E];
+    load_query<Tin, E>(static_cast<const Tin *>(p.q) + h * D + gl * E, qv);
+    const int64_t off = unit * D + gl * E;
+    widen<Tin>(load16(static_cast<const Tin *>(p.k) + off), kf);
+    widen<Tin>(load16(static_cast<const Tin *>(p.v) + off), vf);
+    float *wp = p.w + off;
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c)
+        widen<float>(load16(wp + 4 * c), wv + 4 * c);
+    const float m = p.m[unit], u = p.u[unit];
+
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        part = __builtin_fmaf(qv[e] * p.scale, kf[e], part);
+    const float s = group_sum<L>(part);
+
+    // absorb (s, v): the side with the smaller maximum is scaled by e^{lo-hi}
+    const bool up = s > m;
+    const float hi = up ? s : m;
+    const float lo = up ? m : s;
+    float ex = exp2_fast((lo - hi) * kLog2e);
+    ex = (lo == kNegInf) ? 0.f : ex;
+    const float a = up ? ex : 1.f;
+    const float pr = up ? 1.f : ex;
+    const float nu = __builtin_fmaf(u, a, pr);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        wv[e] = __builtin_fmaf(wv[e], a, pr * vf[e]);
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) {
+        u32x4 x = {__float_as_uint(wv[4 * c]), __float_as_uint(wv[4 * c + 1]),
+                   __float_as_uint(wv[4 * c + 2]), __float_as_uint(wv[4 * c + 3])};
+        store16(wp + 4 * c, x);
+    }
+    if (gl == 0) {
+        p.m[unit] = hi;
+        p.u[unit] = nu;
+    }
+    if (p.o) {
+        const float inv = rcp_fast(nu);
+        float ov[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            ov[e] = wv[e] * inv;
+        store_row<Tout, E>(static_cast<Tout *>(p.o) + off, ov);
+    }
+}
+
+// Empty state: m = -inf, u = 0, w = 0.
+__global__ __launch_bounds__(256) void state_init_kernel(float *m, float *u, float *w,
+                                                         int64_t units, int64_t D)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < units; i += stride) {
+        m[i] = kNegInf;
+        u[i] = 0.f;
+    }
+    const int64_t n4 = units * D / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride)
+        store16(w + 4 * i, u32x4{0, 0, 0, 0});
+}
+
+// Zero a 16-byte aligned buffer whose size is a multiple of 16 bytes, then the tail.
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint8_t *p, size_t bytes)
+{
+    const size_t stride = (size_t)gridDim.x * 256;
+    const size_t n16 = bytes / 16;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
+        store16(p + 16 * i, u32x4{0, 0, 0, 0});
+    const size_t t = n16 * 16 + (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (t < bytes)
+        p[t] = 0;
+}
+
+template <int D, typename Tin, typename Tout>
+static hipError_t step_one(const StepParams &p, hipStream_t stream)
+{
+    constexpr int L = RowGeo<D, Tin>::kLanes;
+    const int64_t threads = p.units * L;
+    const int64_t blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL((step_kernel<D, Tin, Tout>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       p);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t step_dtypes(const StepParams &p, aaren_dtype in, aaren_dtype out,
+                              hipStream_t stream)
+{
+    if (in == AAREN_F32)
+        return out == AAREN_F32 ? step_one<D, float, float>(p, stream)
+                                : step_one<D, float, bf16>(p, stream);
+    return out == AAREN_F32 ? step_one<D, bf16, float>(p, stream)
+                            : step_one<D, bf16, bf16>(p, stream);
+}
+
+hipError_t launch_step(const StepParams &p, int D, aaren_dtype in, aaren_dtype out,
+                       hipStream_t stream)
+{
+    return D == 64 ? step_dtypes<64>(p, in, out, stream) : step_dtypes<128>(p, in, out, stream);
+}
+
+static unsigned grid_for(int64_t work)
+{
+    int64_t b = (work + 255) / 256;
+    if (b > 8192)
+        b = 8192;
+    return (unsigned)(b < 1 ? 1 : b);
+}
+
+hipError_t launch_state_init(float *m, float *u, float *w, int64_t units, int64_t D,
+                             hipStream_t stream)
+{
+    const int64_t work = units * D / 4 > units ? units * D / 4 : units;
+    hipLaunchKernelGGL(state_init_kernel, dim3(grid_for(work)), dim3(256), 0, stream, m, u, w,
+                       units, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream)
+{
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for((int64_t)(bytes / 16) + 1)), dim3(256), 0,
+                       stream, static_cast<uint8_t *>(p), bytes);
+    return hipGetLastError();
+}
+
+}  // namespace aaren

@@ -1,0 +1,161 @@
+/*
+ * libaaren -- exact single-query softmax attention on MI355X (gfx950).
+ *
+ * The library computes attention of ONE query per head over a sequence of
+ * key/value pairs, and its many-to-many form, through the associative
+ * online-softmax combine of a running maximum m, a normaliser u and a
+ * weighted value sum w.
+ *
+ * Sources (the pages these calls implement):
+ *  - "Self-attention Does Not Need O(n^2) Memory" (review), section 1
+ *    Introduction: the attention of a single query is the sum of the values
+ *    weighted by the softmax of the query-key dot products; section 2
+ *    Algorithm: the constant-memory recurrence that accumulates v_i e^{s_i}
+ *    and e^{s_i} in order and divides at the end; section 3 Numerical
+ *    Stability (body lost; read as the running-maximum shift).
+ *  - "Attention as an RNN" (review), abstract items (3) and (4) and the
+ *    proposed method: the many-to-many RNN output computed by a parallel
+ *    prefix scan, one learned query per head (the initial hidden state q),
+ *    constant-memory updates with new tokens.
+ *
+ * Definitions used by every call:
+ *   s_i = scale * <q_h, k_i>                  (scale: caller's, 1/sqrt(d) usual)
+ *   many-to-many:  o_k = sum_{i<=k} e^{s_i} v_i / sum_{i<=k} e^{s_i}
+ *   many-to-one:   o   = o_N
+ *   state (m, u, w): m = max_i s_i, u = sum_i e^{s_i - m}, w = sum_i e^{s_i - m} v_i,
+ *   so that o = w / u and the log-normaliser is L = m + ln u. The empty state
+ *   is (m = -inf, u = 0, w = 0).
+ *
+ * Conventions:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no pointer after a call's work completes.
+ *  - Tensors are dense, row-major, in the shapes given; q, k and v share
+ *    `in_dtype`; every tensor base pointer must be 16-byte aligned.
+ *  - d (head dimension) is 64 or 128.
+ *  - `hip_stream` is a hipStream_t (NULL = the null stream). Every call only
+ *    enqueues work on that stream and returns; device-side faults surface at
+ *    the caller's next synchronisation.
+ *  - Arguments are validated before anything is enqueued: on a non-OK status
+ *    nothing is enqueued and no output is touched; aaren_last_error() then
+ *    holds a description (thread-local).
+ *  - Outputs must not alias inputs.
+ */
+#ifndef AAREN_H
+#define AAREN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum aaren_status {
+    AAREN_OK = 0,
+    AAREN_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad offsets header values */
+    AAREN_ERR_UNSUPPORTED = 2,  /* d not in {64,128}, unknown dtype, size beyond limits */
+    AAREN_ERR_ALIGNMENT = 3,    /* a base pointer not 16-byte aligned */
+    AAREN_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the size query */
+    AAREN_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */
+} aaren_status;
+
+typedef enum aaren_dtype {
+    AAREN_F32 = 0,
+    AAREN_BF16 = 1
+} aaren_dtype;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int aaren_version(void);
+
+/* Static description of a status code. */
+const char *aaren_status_string(aaren_status s);
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char *aaren_last_error(void);
+
+/* ---- workspaces ------------------------------------------------------------
+ * The scans carry the running state across tiles of a sequence through a
+ * caller-owned workspace (per-tile published states and three counters).
+ * Contract:
+ *  - size it with the matching *_workspace_size query;
+ *  - zero it ONCE before its first use (aaren_workspace_clear does that on a
+ *    stream, with a fill kernel); afterwards the library leaves it ready for
+ *    the next call itself -- do not write it between calls;
+ *  - one workspace may be used by aaren_scan and aaren_scan_segmented
+ *    alternately, but by one call at a time: calls that may overlap (different
+ *    streams) need distinct workspaces.
+ * aaren_reduce's workspace holds per-chunk partial states only and needs no
+ * clearing.
+ */
+aaren_status aaren_workspace_clear(void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* ---- many-to-many scan, dense batch ----------------------------------------
+ * Many-to-many output of "Attention as an RNN" (abstract item (3): attention's
+ * many-to-many RNN output by a parallel prefix scan), one query per head.
+ *   q [H,d], k [B,H,N,d], v [B,H,N,d]  (in_dtype)
+ *   o [B,H,N,d]                         (out_dtype), o[b,h,i] = attention of
+ *                                       q[h] over pairs 0..i of (b,h)
+ * B*H*N == 0 is a no-op. Returns WORKSPACE if workspace_bytes is below
+ * aaren_scan_workspace_size(B,H,N,d). */
+size_t aaren_scan_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d);
+aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o,
+                        int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                        aaren_dtype in_dtype, aaren_dtype out_dtype,
+                        void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* ---- many-to-many scan, packed variable-length batch -----------------------
+ * The same output for a packed batch of independent sequences (each one is
+ * scanned on its own; the pages do not treat packed batches, this is the
+ * dense call applied per sequence):
+ *   q [H,d]; k, v, o [T,H,d] token-major (T = total_tokens);
+ *   offsets [num_seqs+1] int64 DEVICE array, offsets[0] = 0, non-decreasing,
+ *   offsets[num_seqs] = T; sequence s holds tokens offsets[s] .. offsets[s+1]-1
+ *   (empty sequences allowed).
+ * The host cannot read device offsets, so only their count is validated; a
+ * decreasing array or one that does not end at T gives unspecified results. */
+size_t aaren_scan_segmented_workspace_size(int64_t num_seqs, int64_t total_tokens,
+                                           int64_t H, int64_t d);
+aaren_status aaren_scan_segmented(const void *q, const void *k, const void *v, void *o,
+                                  const int64_t *offsets, int64_t num_seqs,
+                                  int64_t total_tokens, int64_t H, int64_t d, float scale,
+                                  aaren_dtype in_dtype, aaren_dtype out_dtype,
+                                  void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* ---- constant-memory RNN step ----------------------------------------------
+ * "Attention as an RNN" (abstract item (4)(ii) and method: update with new
+ * tokens in constant memory); the update is the recurrence of section 2 of
+ * the memory-efficient-attention review, stabilised by the running maximum.
+ * Per (stream, head): absorb one pair (k_t, v_t) into the state, in place:
+ *   q [H,d], k_t [S,H,d], v_t [S,H,d]  (in_dtype)
+ *   m [S,H], u [S,H], w [S,H,d]  float32, in/out (m in natural score units)
+ *   o_t [S,H,d] (out_dtype) or NULL: the output after this token, w/u.
+ * aaren_state_init writes the empty state (m = -inf, u = 0, w = 0). */
+aaren_status aaren_state_init(float *m, float *u, float *w, int64_t S, int64_t H, int64_t d,
+                              void *hip_stream);
+aaren_status aaren_step(const void *q, const void *k_t, const void *v_t,
+                        float *m, float *u, float *w, void *o_t,
+                        int64_t S, int64_t H, int64_t d, float scale,
+                        aaren_dtype in_dtype, aaren_dtype out_dtype, void *hip_stream);
+
+/* ---- many-to-one reduction -------------------------------------------------
+ * Single-query attention over all N pairs ("Self-attention Does Not Need
+ * O(n^2) Memory", sections 1-2; "Attention as an RNN", abstract item (1):
+ * the many-to-one RNN output). The pairs are split into chunks whose partial
+ * states are combined at the end; the result does not depend on the order of
+ * the pairs beyond rounding.
+ *   q [H,d], k [B,H,N,d], v [B,H,N,d] (in_dtype);  o [B,H,d] (out_dtype);
+ *   m_out, u_out [B,H] float32 or NULL: the final state's m (natural units)
+ *   and u, so that L = m + ln u.
+ * N == 0 is INVALID_ARG (0/0 has no value); B*H == 0 is a no-op. */
+size_t aaren_reduce_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d);
+aaren_status aaren_reduce(const void *q, const void *k, const void *v, void *o,
+                          float *m_out, float *u_out,
+                          int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                          aaren_dtype in_dtype, aaren_dtype out_dtype,
+                          void *workspace, size_t workspace_bytes, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AAREN_H */

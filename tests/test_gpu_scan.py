@@ -1,0 +1,140 @@
+"""Dense many-to-many scan on the GPU against the CPU oracle.
+
+Sizes span several tiles (256 rows for d=64 fp32 and d=128 bf16, 128 for
+d=128 fp32, 512 for d=64 bf16) with ragged tails."""
+import numpy as np
+import pytest
+import torch
+
+import exact_softmax_attention_02_amd as aaren
+import oracle
+import workloads
+from _gpu import TOL, announce, check, dev, host32, scan_header_error
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.mark.parametrize("d,ind,outd", [(64, "f32", "f32"), (128, "bf16", "f32"),
+                                        (128, "f32", "f32"), (64, "bf16", "f32"),
+                                        (64, "f32", "bf16"), (128, "bf16", "bf16")])
+@pytest.mark.parametrize("B,H,N", [(1, 1, 1), (1, 1, 2), (2, 3, 17), (1, 2, 255), (1, 1, 256),
+                                   (2, 1, 257), (1, 3, 1000), (3, 2, 2049)])
+def test_scan_small(B, H, N, d, ind, outd):
+    announce(f"scan B={B} H={H} N={N} d={d} in={ind} out={outd}")
+    scale = workloads.default_scale(d)
+    q, k, v = workloads.dense_inputs(B, H, N, d, seed=100 + N, device=dev(), dtype=ind)
+    ws = torch.zeros(aaren.aaren_scan_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev())
+    o = aaren.aaren_scan(q, k, v, scale, out_dtype=DT[outd], workspace=ws)
+    ref = oracle.scan(host32(q), host32(k), host32(v), scale)
+    tol = max(TOL[DT[ind]], TOL[DT[outd]])
+    check(o, ref, tol, "scan")
+    assert scan_header_error(ws) == 0
+
+
+def test_scan_single_token_is_exact():
+    announce("scan single token exact")
+    q, k, v = workloads.dense_inputs(4, 8, 1, 64, seed=7, device=dev())
+    o = aaren.aaren_scan(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o, v)
+
+
+def test_scan_equal_scores_running_mean():
+    announce("scan q=0 running mean")
+    _, k, v = workloads.dense_inputs(2, 2, 777, 64, seed=8, device=dev())
+    q = torch.zeros(2, 64, device=dev())
+    o = aaren.aaren_scan(q, k, v)
+    vv = host32(v).astype(np.float64)
+    ref = np.cumsum(vv, axis=2) / np.arange(1, 778)[None, None, :, None]
+    check(o, ref, 1e-5, "running mean")
+
+
+@pytest.mark.parametrize("spread", [80.0, 1000.0])
+def test_scan_large_score_spread(spread):
+    """Scores far beyond exp's range: only a running maximum keeps this finite
+    (and a tile-wide maximum would underflow early rows). The fp32 dot product
+    itself is off by about |s| sqrt(d) 2^-24, which moves every weight by that
+    factor, so the bound scales with the spread: 8 |s| sqrt(d) 2^-24."""
+    announce(f"scan spread {spread}")
+    B, H, N, d = 1, 2, 1500, 64
+    g = torch.Generator(device=dev()).manual_seed(9)
+    q = torch.randn(H, d, generator=g, device=dev())
+    k = torch.randn(B, H, N, d, generator=g, device=dev())
+    v = torch.randn(B, H, N, d, generator=g, device=dev())
+    s = (k @ q[None, :, :, None]).squeeze(-1) * 0.125
+    k = k * (spread / s.abs().amax(-1, keepdim=True))[..., None]
+    o = aaren.aaren_scan(q, k, v, 0.125)
+    ref = oracle.scan(host32(q), host32(k), host32(v), 0.125)
+    check(o, ref, max(1e-5, 8 * spread * d ** 0.5 * 2.0 ** -24), f"spread {spread}")
+
+
+def test_scan_ascending_scores_every_row_a_new_maximum():
+    """Each row raises the running maximum (rescale on every row)."""
+    announce("scan ascending scores")
+    N, d = 600, 64
+    q = torch.zeros(1, d, device=dev())
+    q[0, 0] = 1.0
+    k = torch.zeros(1, 1, N, d, device=dev())
+    k[0, 0, :, 0] = torch.linspace(-300, 300, N, device=dev())
+    v = torch.randn(1, 1, N, d, device=dev(), generator=torch.Generator(device=dev()).manual_seed(3))
+    o = aaren.aaren_scan(q, k, v, 1.0)
+    ref = oracle.scan(host32(q), host32(k), host32(v), 1.0)
+    check(o, ref, 1e-5, "ascending")
+
+
+def test_scan_repeat_is_bitwise_deterministic_and_workspace_reusable():
+    """Thousands of tiles chained by look-back; repeated calls on one workspace
+    (epochs advance) give bitwise-identical results."""
+    announce("scan repeat determinism")
+    B, H, N, d = 2, 2, 65536, 64
+    q, k, v = workloads.dense_inputs(B, H, N, d, seed=11, device=dev())
+    ws = torch.zeros(aaren.aaren_scan_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev())
+    first = aaren.aaren_scan(q, k, v, workspace=ws)
+    for _ in range(20):
+        again = aaren.aaren_scan(q, k, v, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(first, again)
+    assert scan_header_error(ws) == 0
+    epoch = int(ws[0:4].view(torch.int32).item())
+    assert epoch == 21 and int(ws[4:12].view(torch.int32).abs().sum().item()) == 0
+    ref = oracle.scan(host32(q), host32(k), host32(v), workloads.default_scale(d))
+    check(first, ref, 1e-5, "long chain")
+
+
+def test_scan_workspace_shared_by_shapes():
+    """One workspace serves calls of different shapes in turn."""
+    announce("scan workspace across shapes")
+    ws = torch.zeros(aaren.aaren_scan_workspace_size(4, 4, 3000, 128), dtype=torch.uint8,
+                     device=dev())
+    for (B, H, N, d) in [(4, 4, 3000, 128), (1, 1, 5, 64), (2, 3, 999, 64), (4, 4, 3000, 128)]:
+        q, k, v = workloads.dense_inputs(B, H, N, d, seed=N, device=dev())
+        o = aaren.aaren_scan(q, k, v, workspace=ws)
+        ref = oracle.scan(host32(q), host32(k), host32(v), workloads.default_scale(d))
+        check(o, ref, 1e-5, f"shape {(B, H, N, d)}")
+    assert scan_header_error(ws) == 0
+
+
+def test_scan_on_a_side_stream():
+    announce("scan side stream")
+    q, k, v = workloads.dense_inputs(2, 2, 1000, 64, seed=12, device=dev())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o = aaren.aaren_scan(q, k, v)
+    s.synchronize()
+    ref = oracle.scan(host32(q), host32(k), host32(v), workloads.default_scale(64))
+    check(o, ref, 1e-5, "side stream")
+
+
+def test_scan_convex_hull_large():
+    """Property at a size the oracle is not run on: each output coordinate lies
+    within the running min/max of the values."""
+    announce("scan convex hull")
+    q, k, v = workloads.dense_inputs(4, 4, 8192, 64, seed=13, device=dev())
+    o = aaren.aaren_scan(q, k, v)
+    lo = torch.cummin(v, dim=2).values
+    hi = torch.cummax(v, dim=2).values
+    torch.cuda.synchronize()
+    assert bool(((o >= lo - 1e-5) & (o <= hi + 1e-5)).all())

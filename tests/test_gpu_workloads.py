@@ -1,0 +1,129 @@
+"""Every named workload at full size, in the launch configuration the
+benchmark times, against the CPU oracle: in full where the oracle runs in
+seconds (single, dense, long_bf16, reduce), on sampled sequences / streams
+otherwise (ragged, stream)."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import exact_softmax_attention_02_amd as aaren
+import oracle
+import workloads
+from _gpu import TOL, announce, check, dev, host32, scan_header_error
+
+pytestmark = pytest.mark.gpu
+W = workloads.WORKLOADS
+
+
+@pytest.fixture(autouse=True)
+def _free():
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["single", "dense"])
+def test_dense_workloads_in_full(name):
+    w = W[name]
+    sz = w.sizes
+    announce(f"workload {name}: {w.describe()}")
+    q, k, v = workloads.dense_inputs(sz["B"], sz["H"], sz["N"], sz["d"], w.seed, device=dev())
+    scale = workloads.default_scale(sz["d"])
+    o = aaren.aaren_scan(q, k, v, scale)
+    ref = oracle.scan(host32(q), host32(k), host32(v), scale)
+    err = check(o, ref, TOL[torch.float32], name)
+    print(f"{name}: max scaled err {err:.3e}")
+
+
+def test_long_bf16_in_full():
+    w = W["long_bf16"]
+    sz = w.sizes
+    announce(f"workload long_bf16: {w.describe()}")
+    q, k, v = workloads.dense_inputs(sz["B"], sz["H"], sz["N"], sz["d"], w.seed, device=dev(),
+                                     dtype="bf16", score_span=w.score_span)
+    scale = workloads.default_scale(sz["d"])
+    ws = torch.zeros(aaren.aaren_scan_workspace_size(*k.shape), dtype=torch.uint8, device=dev())
+    o = aaren.aaren_scan(q, k, v, scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert scan_header_error(ws) == 0
+    qh = host32(q)
+    worst = 0.0
+    for b in range(sz["B"]):  # one batch row at a time keeps host memory small
+        ref = oracle.scan(qh, host32(k[b:b + 1]), host32(v[b:b + 1]), scale)
+        worst = max(worst, check(o[b:b + 1], ref, TOL[torch.bfloat16], f"long_bf16 b={b}"))
+    print(f"long_bf16: max scaled err {worst:.3e}")
+
+
+def test_ragged_sampled_sequences():
+    w = W["ragged"]
+    sz = w.sizes
+    announce(f"workload ragged: {w.describe()}")
+    lengths = workloads.segment_lengths(sz["num_seqs"], sz["max_len"], w.seed)
+    q, k, v, offs = workloads.segmented_inputs(lengths, sz["H"], sz["d"], w.seed, device=dev())
+    scale = workloads.default_scale(sz["d"])
+    T = int(lengths.sum())
+    ws = torch.zeros(aaren.aaren_scan_segmented_workspace_size(len(lengths), T, sz["H"], sz["d"]),
+                     dtype=torch.uint8, device=dev())
+    o = aaren.aaren_scan_segmented(q, k, v, offs, scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert scan_header_error(ws) == 0
+    ho = offs.cpu().numpy()
+    rng = np.random.default_rng(123)
+    pick = set(rng.choice(len(lengths), 40, replace=False).tolist())
+    pick |= {0, 1, 2, len(lengths) - 1, int(lengths.argmax()), int(lengths.argmin())}
+    qh = host32(q)
+    worst = 0.0
+    for s in sorted(pick):
+        a, b = int(ho[s]), int(ho[s + 1])
+        ref = oracle.scan_segmented(qh, host32(k[a:b]), host32(v[a:b]), np.array([0, b - a]), scale)
+        worst = max(worst, check(o[a:b], ref, TOL[torch.float32], f"ragged sequence {s}"))
+    # a contiguous run of sequences, crossing many tile boundaries
+    a, b = int(ho[100]), int(ho[140])
+    ref = oracle.scan_segmented(qh, host32(k[a:b]), host32(v[a:b]), ho[100:141] - a, scale)
+    worst = max(worst, check(o[a:b], ref, TOL[torch.float32], "ragged sequences 100..139"))
+    print(f"ragged: T={T} max scaled err over sampled sequences {worst:.3e}")
+
+
+def test_stream_sampled_streams():
+    w = W["stream"]
+    sz = w.sizes
+    S, H, d, T = sz["S"], sz["H"], sz["d"], sz["steps"]
+    announce(f"workload stream: {w.describe()}")
+    q, k, v = workloads.step_inputs(S, H, d, T, w.seed, device=dev())
+    scale = workloads.default_scale(d)
+    m, u, ww = aaren.new_state(S, H, d, device=dev())
+    o = torch.empty(S, H, d, device=dev())
+    sample = torch.from_numpy(np.sort(np.random.default_rng(5).choice(S, 512, replace=False))).to(dev())
+    kept = []
+    for t in range(T):
+        aaren.aaren_step(q, k[t], v[t], m, u, ww, scale, o_t=o)
+        kept.append(o[sample].clone())
+    got = torch.stack(kept)                      # [T, 512, H, d]
+    ks, vs = host32(k[:, sample]), host32(v[:, sample])
+    del k, v
+    st = oracle.state_init(len(sample), H, d)
+    qh = host32(q)
+    worst = 0.0
+    for t in range(T):
+        ref = oracle.step(qh, ks[t], vs[t], st, scale)
+        worst = max(worst, check(got[t], ref, TOL[torch.float32], f"stream step {t}"))
+    L = host32(m[sample]).astype(np.float64) + np.log(host32(u[sample]).astype(np.float64))
+    Lr = st[0] + np.log(st[1])
+    assert np.max(np.abs(L - Lr) / (1 + np.abs(Lr))) <= 1e-5
+    print(f"stream: max scaled err over 512 sampled streams x {T} steps {worst:.3e}")
+
+
+def test_reduce_in_full():
+    w = W["reduce"]
+    sz = w.sizes
+    announce(f"workload reduce: {w.describe()}")
+    q, k, v = workloads.reduce_inputs(sz["B"], sz["H"], sz["N"], sz["d"], w.seed, device=dev())
+    scale = workloads.default_scale(sz["d"])
+    o, m, u = aaren.aaren_reduce(q, k, v, scale, stats=True)
+    ref, rm, rl = oracle.reduce(host32(q), host32(k), host32(v), scale, stats=True)
+    err = check(o, ref, TOL[torch.float32], "reduce")
+    L = host32(m).astype(np.float64) + np.log(host32(u).astype(np.float64))
+    assert np.max(np.abs(L - rl) / (1 + np.abs(rl))) <= 1e-5
+    print(f"reduce: max scaled err {err:.3e}")
