@@ -159,6 +159,23 @@ __device__ __forceinline__ void merge_weights(float ma, float mb, float &m, floa
     m = hi;
 }
 
+// (m,u,w) = (m_a,u_a,w_a) (+) (m_b,u_b,w_b) over N columns, the earlier state
+// on the left. Written with explicit fma so that every call site rounds the
+// same way (the scan's cross-tile carry relies on that to be reproducible).
+// w may alias aw or bw.
+template <int N>
+__device__ __forceinline__ void combine(float am, float au, const float *aw, float bm, float bu,
+                                        const float *bw, float &m, float &u, float *w)
+{
+    float fa, fb, mm;
+    merge_weights(am, bm, mm, fa, fb);
+    u = __builtin_fmaf(fa, au, fb * bu);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        w[i] = __builtin_fmaf(fa, aw[i], fb * bw[i]);
+    m = mm;
+}
+
 // 64-bit agent-scope relaxed accesses (coherent across the XCDs' L2s).
 __device__ __forceinline__ void st_agent(uint64_t *p, uint64_t v)
 {

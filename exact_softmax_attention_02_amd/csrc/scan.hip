@@ -50,6 +50,9 @@ struct ScanShape {
     static_assert(D % 64 == 0, "d = 64 or 128");
 };
 
+// Aggregates a look-back walk may park before it waits for a prefix.
+constexpr int kWindow = 16;
+
 __device__ __forceinline__ uint32_t next_epoch(uint32_t prev)
 {
     uint32_t e = prev + 1;
@@ -94,6 +97,9 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     __shared__ __attribute__((aligned(16))) float sh_gw[NG][D];
     __shared__ float sh_cm, sh_cu;
     __shared__ __attribute__((aligned(16))) float sh_cw[D];
+    // aggregates met on the look-back walk, newest first (wave 0 only)
+    __shared__ float sh_win_m[kWindow], sh_win_u[kWindow];
+    __shared__ float sh_win_w[kWindow][D];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -219,10 +225,10 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
             fa = bf ? 0.f : fa;  // a sequence start in g cuts what came before
             fb = bf ? 1.f : fb;
             m = bf ? bm : m;
-            xu = fa * xu + fb * bu;
+            xu = __builtin_fmaf(fa, xu, fb * bu);
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                xw[e] = fa * xw[e] + fb * sh_gw[g][gl * E + e];
+                xw[e] = __builtin_fmaf(fa, xw[e], fb * sh_gw[g][gl * E + e]);
             xm = m;
             xf = xf || bf;
         }
@@ -248,10 +254,10 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
             fa = bf ? 0.f : fa;
             fb = bf ? 1.f : fb;
             m = bf ? bm : m;
-            au = fa * au + fb * bu;
+            au = __builtin_fmaf(fa, au, fb * bu);
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                aw[c] = fa * aw[c] + fb * sh_gw[g][lane + 64 * c];
+                aw[c] = __builtin_fmaf(fa, aw[c], fb * sh_gw[g][lane + 64 * c]);
             am = m;
             af = af || bf;
         }
@@ -272,8 +278,14 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
                 publish<D>(my, epoch << 1, am, au, aw, lane);
             else
                 publish<D>(my, (epoch << 1) | 1u, am, au, aw, lane);
+            // Walk back to the nearest predecessor with an inclusive prefix (or,
+            // packed batches, an aggregate that holds a sequence start), parking
+            // the aggregates met on the way; then fold them onto it oldest first.
+            // The carry is thus always the left fold A_0 (+) ... (+) A_{j-1},
+            // whatever the timing, and the results are reproducible bit for bit.
             int64_t pred = (int64_t)ticket - p.streams;
             uint32_t polls = 0;
+            int parked = 0;
             while (true) {
                 const uint64_t *agg = p.slots + (size_t)pred * 2 * SLOT;
                 const uint64_t *pre = agg + SLOT;
@@ -294,25 +306,29 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
                 }
                 pre_ok = __all(pre_ok);
                 agg_ok = __all(agg_ok);
-                if (pre_ok || agg_ok) {
-                    const float bm = word_value(pre_ok ? pmw : amw);
-                    const float bu = word_value(pre_ok ? puw : auw);
-                    float m, fx, fc;  // the earlier tile goes on the left
-                    merge_weights(bm, cm, m, fx, fc);
-                    cu = fx * bu + fc * cu;
+                const bool agg_starts = SEG && agg_ok && ((amw >> 32) & 1u);
+                if (pre_ok || agg_starts) {
+                    cm = word_value(pre_ok ? pmw : amw);
+                    cu = word_value(pre_ok ? puw : auw);
 #pragma unroll
                     for (int c = 0; c < CPL; ++c)
-                        cw[c] = fx * word_value(pre_ok ? wp[c] : wa[c]) + fc * cw[c];
-                    cm = m;
-                    const bool stop = pre_ok || (SEG && ((amw >> 32) & 1u));
-                    if (stop)
-                        break;
+                        cw[c] = word_value(pre_ok ? wp[c] : wa[c]);
+                    break;
+                }
+                if (agg_ok && parked < kWindow) {
                     if (pred < p.streams) {  // a first tile never publishes an aggregate
                         if (lane == 0)
                             __hip_atomic_fetch_or(p.header + kError, 2u, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
+                    // every lane writes the same m, u and reads back only what it wrote
+                    sh_win_m[parked] = word_value(amw);
+                    sh_win_u[parked] = word_value(auw);
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c)
+                        sh_win_w[parked][lane + 64 * c] = word_value(wa[c]);
+                    ++parked;
                     pred -= p.streams;
                     continue;
                 }
@@ -324,21 +340,21 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
+            for (int i = parked - 1; i >= 0; --i) {
+                float yw[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    yw[c] = sh_win_w[i][lane + 64 * c];
+                combine<CPL>(cm, cu, cw, sh_win_m[i], sh_win_u[i], yw, cm, cu, cw);
+            }
         }
         // inclusive prefix = carry (+) aggregate, unless the tile holds a start
         float im = am, iu = au, iw[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
             iw[c] = aw[c];
-        if (!af) {
-            float m, fa, fb;
-            merge_weights(cm, am, m, fa, fb);
-            iu = fa * cu + fb * au;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                iw[c] = fa * cw[c] + fb * aw[c];
-            im = m;
-        }
+        if (!af)
+            combine<CPL>(cm, cu, cw, am, au, aw, im, iu, iw);
         publish<D>(my + SLOT, epoch << 1, im, iu, iw, lane);
 
         if (lane == 0) {
@@ -358,14 +374,11 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     for (int e = 0; e < E; ++e)
         xw[e] = pw[e];
     if (!pf) {
-        const float cm = sh_cm, cu = sh_cu;
-        float m, fa, fb;
-        merge_weights(cm, pm, m, fa, fb);
-        xu = fa * cu + fb * pu;
+        float cw[E];
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            xw[e] = fa * sh_cw[gl * E + e] + fb * pw[e];
-        xm = m;
+            cw[e] = sh_cw[gl * E + e];
+        combine<E>(sh_cm, sh_cu, cw, pm, pu, pw, xm, xu, xw);
     }
 
     Tout *op = static_cast<Tout *>(p.o) + base;

@@ -9,7 +9,7 @@ import torch
 import exact_softmax_attention_02_amd as aaren
 import oracle
 import workloads
-from _gpu import TOL, announce, check, dev, host32, scan_header_error
+from _gpu import TOL, TOL_BF16_OUT, announce, check, dev, host32, scan_header_error
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,7 @@ def test_scan_small(B, H, N, d, ind, outd):
     ws = torch.zeros(aaren.aaren_scan_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev())
     o = aaren.aaren_scan(q, k, v, scale, out_dtype=DT[outd], workspace=ws)
     ref = oracle.scan(host32(q), host32(k), host32(v), scale)
-    tol = max(TOL[DT[ind]], TOL[DT[outd]])
+    tol = TOL_BF16_OUT if outd == "bf16" else TOL[DT[ind]]
     check(o, ref, tol, "scan")
     assert scan_header_error(ws) == 0
 
@@ -71,7 +71,9 @@ def test_scan_large_score_spread(spread):
 
 
 def test_scan_ascending_scores_every_row_a_new_maximum():
-    """Each row raises the running maximum (rescale on every row)."""
+    """Each row raises the running maximum (rescale on every row). Scores reach
+    |s| = 300, so fp32 score rounding (about |s| 2^-24 per score, one nonzero
+    coordinate per dot product) bounds the error: 8 |s| 2^-24."""
     announce("scan ascending scores")
     N, d = 600, 64
     q = torch.zeros(1, d, device=dev())
@@ -81,7 +83,7 @@ def test_scan_ascending_scores_every_row_a_new_maximum():
     v = torch.randn(1, 1, N, d, device=dev(), generator=torch.Generator(device=dev()).manual_seed(3))
     o = aaren.aaren_scan(q, k, v, 1.0)
     ref = oracle.scan(host32(q), host32(k), host32(v), 1.0)
-    check(o, ref, 1e-5, "ascending")
+    check(o, ref, max(1e-5, 8 * 300 * 2.0 ** -24), "ascending")
 
 
 def test_scan_repeat_is_bitwise_deterministic_and_workspace_reusable():
