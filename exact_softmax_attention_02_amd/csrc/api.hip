@@ -1,9 +1,12 @@
 // C ABI of libaaren: argument validation, workspace sizing and dispatch.
 // Every check runs before anything is enqueued, so a non-OK status leaves the
 // outputs untouched. The kernels live in scan.hip, step.hip and reduce.hip.
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
+#include <unordered_map>
 
 #include "layout.h"
 
@@ -39,11 +42,6 @@ bool aligned16(const void *p)
 bool dtype_ok(aaren_dtype t)
 {
     return t == AAREN_F32 || t == AAREN_BF16;
-}
-
-size_t dtype_bytes(aaren_dtype t)
-{
-    return t == AAREN_F32 ? 4 : 2;
 }
 
 // a*b*... without overflow past 2^62, else -1
@@ -93,15 +91,56 @@ aaren_status check_ptr(const void *p, const char *name)
             return st_;                      \
     } while (0)
 
-size_t scan_workspace_bytes(int64_t tiles, int64_t bitmap_words, int64_t d)
+size_t counter_bytes(int64_t streams)
 {
-    return aaren::kHeaderBytes + aaren::round256((size_t)bitmap_words * 4) +
+    return aaren::round256((size_t)streams * aaren::kCounterStride * 4);
+}
+
+size_t scan_workspace_bytes(int64_t streams, int64_t tiles, int64_t bitmap_words, int64_t d)
+{
+    return aaren::kHeaderBytes + counter_bytes(streams) +
+           aaren::round256((size_t)bitmap_words * 4) +
            (size_t)tiles * 2 * aaren::slot_words((int)d) * 8;
+}
+
+// Each scan call tags what it publishes with an epoch no other call of this
+// process uses (1 .. 2^31-2, wrapping after 2^31-2 calls).
+uint32_t next_epoch()
+{
+    static std::atomic<uint32_t> counter{0};
+    return counter.fetch_add(1, std::memory_order_relaxed) % 0x7ffffffeu + 1u;
 }
 
 int64_t ceil_div(int64_t a, int64_t b)
 {
     return (a + b - 1) / b;
+}
+
+// The ticket counters sit right after the header and their number depends on
+// the call's shape; a call's tile slots start where its counters end. Each
+// call leaves its own counters at zero, but its slots may cover bytes that a
+// later call with more streams uses as counters. So the library remembers,
+// per workspace, how many counter bytes are known to be zero (all of them for
+// a workspace it has not seen: it was zero-filled, by contract) and clears the
+// counter region before a call that needs more than that.
+std::mutex g_ws_mutex;
+std::unordered_map<const void *, size_t> g_ws_clean;
+
+aaren_status prepare_counters(void *workspace, size_t need, hipStream_t stream)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto it = g_ws_clean.find(workspace);
+    const size_t clean = it == g_ws_clean.end() ? SIZE_MAX : it->second;
+    if (need > clean) {
+        aaren_status st = hip_status(
+            aaren::launch_fill_zero(static_cast<uint8_t *>(workspace) + aaren::kHeaderBytes, need,
+                                    stream),
+            "counter clear launch");
+        if (st != AAREN_OK)
+            return st;
+    }
+    g_ws_clean[workspace] = need;
+    return AAREN_OK;
 }
 
 }  // namespace
@@ -135,9 +174,12 @@ AAREN_API aaren_status aaren_workspace_clear(void *workspace, size_t workspace_b
     if (workspace_bytes == 0)
         return AAREN_OK;
     CHECK(check_ptr(workspace, "workspace"));
-    return hip_status(aaren::launch_fill_zero(workspace, workspace_bytes,
-                                              static_cast<hipStream_t>(hip_stream)),
-                      "workspace clear launch");
+    CHECK(hip_status(aaren::launch_fill_zero(workspace, workspace_bytes,
+                                             static_cast<hipStream_t>(hip_stream)),
+                     "workspace clear launch"));
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    g_ws_clean[workspace] = SIZE_MAX;
+    return AAREN_OK;
 }
 
 // ---- dense scan ---------------------------------------------------------------
@@ -149,7 +191,7 @@ AAREN_API size_t aaren_scan_workspace_size(int64_t B, int64_t H, int64_t N, int6
     const int64_t tiles = mul_checked({B, H, ceil_div(N, aaren::scan_tile_rows_min((int)d))});
     if (tiles < 0)
         return 0;
-    return scan_workspace_bytes(tiles, 0, d);
+    return scan_workspace_bytes(B * H, tiles, 0, d);
 }
 
 AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, int64_t B,
@@ -176,7 +218,7 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
     if (tiles >= 0x7fffffff)
         return fail(AAREN_ERR_UNSUPPORTED, "%lld tiles exceed the 2^31-1 launch limit",
                     (long long)tiles);
-    const size_t need = scan_workspace_bytes(tiles, 0, d);
+    const size_t need = scan_workspace_bytes(B * H, tiles, 0, d);
     if (!workspace || workspace_bytes < need)
         return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
                     need);
@@ -197,14 +239,18 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
     p.row_stride = d;
     p.chunks = chunks;
     p.num_tiles = (uint32_t)tiles;
+    p.epoch = next_epoch();
     p.qscale = scale * 1.44269504088896340736f;
-    p.header = static_cast<uint32_t *>(workspace);
-    p.slots = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(workspace) + aaren::kHeaderBytes);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    p.header = reinterpret_cast<uint32_t *>(ws);
+    p.counters = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes);
+    p.slots = reinterpret_cast<uint64_t *>(ws + aaren::kHeaderBytes + counter_bytes(B * H));
     if (log_enabled())
         fprintf(stderr, "[aaren] scan B=%lld H=%lld N=%lld d=%lld tiles=%lld rows/tile=%d\n",
                 (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles, rows);
-    return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, false,
-                                         static_cast<hipStream_t>(hip_stream)),
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    CHECK(prepare_counters(workspace, counter_bytes(B * H), st));
+    return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, false, st),
                       "scan launch");
 }
 
@@ -218,7 +264,7 @@ AAREN_API size_t aaren_scan_segmented_workspace_size(int64_t num_seqs, int64_t t
     const int64_t tiles = mul_checked({H, ceil_div(total_tokens, aaren::scan_tile_rows_min((int)d))});
     if (tiles < 0)
         return 0;
-    return scan_workspace_bytes(tiles, ceil_div(total_tokens, 32), d);
+    return scan_workspace_bytes(H, tiles, ceil_div(total_tokens, 32), d);
 }
 
 AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const void *v, void *o,
@@ -254,7 +300,7 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
         return fail(AAREN_ERR_UNSUPPORTED, "%lld tiles exceed the 2^31-1 launch limit",
                     (long long)tiles);
     const int64_t words = ceil_div(total_tokens, 32);
-    const size_t need = scan_workspace_bytes(tiles, words, d);
+    const size_t need = scan_workspace_bytes(H, tiles, words, d);
     if (!workspace || workspace_bytes < need)
         return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
                     need);
@@ -262,7 +308,7 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
         return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
 
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    uint32_t *bitmap = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes);
+    uint32_t *bitmap = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes + counter_bytes(H));
     aaren::ScanParams p{};
     p.q = q;
     p.k = k;
@@ -277,15 +323,18 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
     p.row_stride = H * d;
     p.chunks = chunks;
     p.num_tiles = (uint32_t)tiles;
+    p.epoch = next_epoch();
     p.qscale = scale * 1.44269504088896340736f;
-    p.header = static_cast<uint32_t *>(workspace);
-    p.slots = reinterpret_cast<uint64_t *>(ws + aaren::kHeaderBytes +
+    p.header = reinterpret_cast<uint32_t *>(ws);
+    p.counters = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes);
+    p.slots = reinterpret_cast<uint64_t *>(ws + aaren::kHeaderBytes + counter_bytes(H) +
                                            aaren::round256((size_t)words * 4));
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     if (log_enabled())
         fprintf(stderr, "[aaren] scan_segmented S=%lld T=%lld H=%lld d=%lld tiles=%lld\n",
                 (long long)num_seqs, (long long)total_tokens, (long long)H, (long long)d,
                 (long long)tiles);
+    CHECK(prepare_counters(workspace, counter_bytes(H), st));
     CHECK(hip_status(aaren::launch_segment_flags(offsets, num_seqs, total_tokens, bitmap, words, st),
                      "segment flag launch"));
     return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, true, st),

@@ -12,26 +12,26 @@
 namespace aaren {
 
 // ---- scan workspace ---------------------------------------------------------
-// [ header: 64 x u32 ][ segment-start bitmap (segmented scan only) ][ tile slots ]
-// header[kEpoch]  : epoch of the last completed call (0 after clearing)
-// header[kTicket] : next tile ticket of the running call (0 between calls)
-// header[kDone]   : tiles finished by the running call (0 between calls)
-// header[kError]  : set (never cleared by a call) when a tile gave up waiting
-//                   for its predecessors or found the counters inconsistent --
-//                   only possible with a workspace that was not zero-filled
-//                   before first use or was shared by overlapping calls
+// [ header: 256 B ][ ticket counters ][ segment-start bitmap (segmented only) ][ tile slots ]
+// header[kError] : set (never cleared by a call) when a tile gave up waiting
+//                  for its predecessors or drew a ticket out of range -- only
+//                  possible with a workspace that was not zero-filled before
+//                  first use or was shared by overlapping calls.
+// Ticket counters: one per stream, each in its own 128-byte line. A tile's
+//   workgroup draws its position along the stream from its stream's counter
+//   with a wrapping increment, so the counter is back at 0 when the call ends.
 // Tile slots: per tile two published states ("aggregate" then "inclusive
-// prefix"), each kSlotWords(D) 64-bit words: word 0 = m, word 1 = u, words
-// 2.. = w[0..D-1]. A word is (tag << 32) | float bits, tag = epoch << 1 | flag,
-// so a reader can tell a word of the running call from a stale one without
-// any fence; flag marks an aggregate that contains a sequence start.
-constexpr int kEpoch = 0;
-constexpr int kTicket = 1;
-constexpr int kDone = 2;
+//   prefix"), each slot_words(D) 64-bit words: word 0 = m, word 1 = u, words
+//   2.. = w[0..D-1]. A word is (tag << 32) | float bits, tag = epoch << 1 |
+//   flag, where the epoch is unique to each call of the process; a reader thus
+//   tells a word of the running call from a stale one without any fence, and
+//   the slots never need resetting. flag marks an aggregate that contains a
+//   sequence start.
 constexpr int kError = 3;
+constexpr size_t kHeaderBytes = 256;
+constexpr int kCounterStride = 32;  // u32 words between ticket counters (128 B)
 // polls of a predecessor's slots before a tile gives up (about a second)
 constexpr uint32_t kMaxPolls = 1u << 20;
-constexpr size_t kHeaderBytes = 256;
 
 __host__ __device__ constexpr int slot_words(int D)
 {
@@ -72,8 +72,10 @@ struct ScanParams {
     int64_t row_stride;      // elements between rows of a stream: d or H*d
     int64_t chunks;          // tiles per stream
     uint32_t num_tiles;
+    uint32_t epoch;          // unique to this call (1 .. 2^31-2)
     float qscale;            // scale * log2(e)
     uint32_t *header;
+    uint32_t *counters;      // [streams * kCounterStride]
     uint64_t *slots;
 };
 

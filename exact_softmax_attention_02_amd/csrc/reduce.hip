@@ -68,8 +68,8 @@ __global__ __launch_bounds__(64 * WAVES) void reduce_partial_kernel(const Reduce
             kr[r] = u32x4{0, 0, 0, 0};
             vr[r] = u32x4{0, 0, 0, 0};
             if (r < nvalid) {
-                kr[r] = load16(kb + (row0 + r) * D);
-                vr[r] = load16(vb + (row0 + r) * D);
+                kr[r] = load16_stream(kb + (row0 + r) * D);
+                vr[r] = load16_stream(vb + (row0 + r) * D);
             }
         }
         float s[R];

@@ -20,10 +20,11 @@
 //    sums, so no chained rescaling); the groups' states go through LDS.
 //  * Cross-tile carry by decoupled look-back: a tile publishes its aggregate
 //    state at once, then walks back over predecessor tiles of its stream until
-//    one has published an inclusive prefix, and publishes its own. Tiles take
-//    tickets in launch order from a counter, so a tile only ever waits for
-//    tiles that already run. Published words carry an epoch tag, so readers
-//    need no fence and the workspace never has to be reset between calls.
+//    one has published an inclusive prefix, and publishes its own. A tile's
+//    position along its stream comes from a per-stream ticket counter, so a
+//    tile only ever waits for tiles that already run, and the counters do not
+//    contend. Published words carry the call's epoch, so readers need no
+//    fence and the slots never have to be reset between calls.
 //  * Pass 2 re-runs each group's rows from its exclusive prefix with a running
 //    maximum (outputs need the per-row maximum: a shared tile maximum would
 //    underflow early rows when scores span more than ~87), normalises and
@@ -52,12 +53,6 @@ struct ScanShape {
 
 // Aggregates a look-back walk may park before it waits for a prefix.
 constexpr int kWindow = 16;
-
-__device__ __forceinline__ uint32_t next_epoch(uint32_t prev)
-{
-    uint32_t e = prev + 1;
-    return (e >= 0x7fffffffu) ? 1u : e;
-}
 
 __device__ __forceinline__ bool tag_ok(uint64_t word, uint32_t epoch)
 {
@@ -91,7 +86,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     constexpr int E = S::E, L = S::L, GPW = S::GPW, NG = S::NG, ROWS = S::ROWS;
     constexpr int SLOT = S::SLOT, CPL = S::CPL;
 
-    __shared__ uint32_t sh_ticket, sh_epoch;
+    __shared__ uint32_t sh_chunk;
     __shared__ float sh_gm[NG], sh_gu[NG];
     __shared__ uint32_t sh_gf[NG];
     __shared__ __attribute__((aligned(16))) float sh_gw[NG][D];
@@ -106,23 +101,25 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     const int gl = lane % L;                     // lane within its group
     const int grp = wave * GPW + lane / L;       // group within the tile
 
-    if (tid == 0) {
-        sh_ticket = __hip_atomic_fetch_add(p.header + kTicket, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-        sh_epoch = next_epoch(__hip_atomic_load(p.header + kEpoch, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT));
-    }
+    // Workgroup b works on stream b % streams and draws its position along the
+    // stream from that stream's counter, so a tile only ever waits for tiles
+    // whose workgroups already run (no reliance on dispatch order).
+    const uint32_t stream32 = blockIdx.x % (uint32_t)p.streams;
+    if (tid == 0)
+        sh_chunk = __builtin_amdgcn_atomic_inc32(p.counters + (size_t)stream32 * kCounterStride,
+                                                 (uint32_t)(p.chunks - 1), __ATOMIC_RELAXED,
+                                                 "agent");
     __syncthreads();
-    const uint32_t ticket = __builtin_amdgcn_readfirstlane(sh_ticket);
-    const uint32_t epoch = __builtin_amdgcn_readfirstlane(sh_epoch);
-    if (ticket >= p.num_tiles) {  // counters were not left at zero: refuse to run
+    const uint32_t chunk32 = __builtin_amdgcn_readfirstlane(sh_chunk);
+    const uint32_t epoch = p.epoch;
+    if (chunk32 >= (uint32_t)p.chunks) {  // counter not at zero: refuse to run
         if (tid == 0)
             __hip_atomic_fetch_or(p.header + kError, 1u, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    const int64_t chunk = ticket / p.streams;
-    const int64_t stream = ticket - chunk * p.streams;
+    const int64_t chunk = chunk32, stream = stream32;
+    const int64_t tile = chunk * p.streams + stream;          // slot index
     const int64_t row0 = chunk * ROWS + (int64_t)grp * R;   // first row of this group
     const int64_t left = p.rows - row0;
     const int nvalid = left <= 0 ? 0 : (left >= R ? R : (int)left);
@@ -137,8 +134,8 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
         kr[r] = u32x4{0, 0, 0, 0};
         vr[r] = u32x4{0, 0, 0, 0};
         if (r < nvalid) {
-            kr[r] = load16(kp + r * p.row_stride);
-            vr[r] = load16(vp + r * p.row_stride);
+            kr[r] = load16_stream(kp + r * p.row_stride);
+            vr[r] = load16_stream(vp + r * p.row_stride);
         }
     }
 
@@ -262,7 +259,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
             af = af || bf;
         }
 
-        uint64_t *my = p.slots + (size_t)ticket * 2 * SLOT;
+        uint64_t *my = p.slots + (size_t)tile * 2 * SLOT;
         float cm = kNegInf, cu = 0.f, cw[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
@@ -283,7 +280,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
             // the aggregates met on the way; then fold them onto it oldest first.
             // The carry is thus always the left fold A_0 (+) ... (+) A_{j-1},
             // whatever the timing, and the results are reproducible bit for bit.
-            int64_t pred = (int64_t)ticket - p.streams;
+            int64_t pred = tile - p.streams;
             uint32_t polls = 0;
             int parked = 0;
             while (true) {
@@ -416,17 +413,6 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
         }
     }
 
-    // ---- the last tile of the call leaves the counters ready for the next -----
-    if (tid == 0) {
-        const uint32_t n = __hip_atomic_fetch_add(p.header + kDone, 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-        if (n == p.num_tiles - 1) {
-            __hip_atomic_store(p.header + kTicket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(p.header + kDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(p.header + kEpoch, epoch, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
 }
 
 // One thread per 32-row bitmap word: bit b of word i is set when row 32i+b is

@@ -26,8 +26,8 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p)
     float qv[E], kf[E], vf[E], wv[E];
     load_query<Tin, E>(static_cast<const Tin *>(p.q) + h * D + gl * E, qv);
     const int64_t off = unit * D + gl * E;
-    widen<Tin>(load16(static_cast<const Tin *>(p.k) + off), kf);
-    widen<Tin>(load16(static_cast<const Tin *>(p.v) + off), vf);
+    widen<Tin>(load16_stream(static_cast<const Tin *>(p.k) + off), kf);
+    widen<Tin>(load16_stream(static_cast<const Tin *>(p.v) + off), vf);
     float *wp = p.w + off;
 #pragma unroll
     for (int c = 0; c < E / 4; ++c)

@@ -75,15 +75,19 @@ const char *aaren_last_error(void);
 
 /* ---- workspaces ------------------------------------------------------------
  * The scans carry the running state across tiles of a sequence through a
- * caller-owned workspace (per-tile published states and three counters).
+ * caller-owned workspace (per-stream ticket counters and per-tile published
+ * states, tagged with a per-call epoch).
  * Contract:
  *  - size it with the matching *_workspace_size query;
  *  - zero it ONCE before its first use (aaren_workspace_clear does that on a
  *    stream, with a fill kernel); afterwards the library leaves it ready for
- *    the next call itself -- do not write it between calls;
- *  - one workspace may be used by aaren_scan and aaren_scan_segmented
- *    alternately, but by one call at a time: calls that may overlap (different
- *    streams) need distinct workspaces.
+ *    the next call itself (it remembers, per workspace address, which part is
+ *    known clean, and clears its counters again only when a call of another
+ *    shape needs it) -- do not write it between calls, and zero it again if
+ *    its memory is handed out anew;
+ *  - calls of any shape, dense or packed, may share one workspace, but only
+ *    one call at a time: calls that may overlap (different streams) need
+ *    distinct workspaces.
  * aaren_reduce's workspace holds per-chunk partial states only and needs no
  * clearing.
  */

@@ -48,11 +48,13 @@ def test_version_and_strings():
 
 def test_workspace_sizes():
     # dense d=64: 256-row tiles, two published states of 72 words per tile
-    assert aaren.aaren_scan_workspace_size(32, 8, 4096, 64) == 256 + 32 * 8 * 16 * 2 * 72 * 8
-    assert aaren.aaren_scan_workspace_size(1, 1, 0, 64) == 256
+    # header + one 128-byte ticket counter per stream + two states per tile
+    assert aaren.aaren_scan_workspace_size(32, 8, 4096, 64) == \
+        256 + 256 * 128 + 32 * 8 * 16 * 2 * 72 * 8
+    assert aaren.aaren_scan_workspace_size(1, 1, 0, 64) == 256 + 256
     assert aaren.aaren_scan_workspace_size(1, 1, 10, 63) == 0
     seg = aaren.aaren_scan_segmented_workspace_size(3, 1000, 8, 64)
-    assert seg == 256 + 256 + 8 * 4 * 2 * 72 * 8
+    assert seg == 256 + 1024 + 256 + 8 * 4 * 2 * 72 * 8
     assert aaren.aaren_reduce_workspace_size(1, 1, 1 << 20, 128) == 1024 * 136 * 4
 
 
