@@ -81,11 +81,30 @@ def make(name: str, device):
     import exact_softmax_attention_02_amd as aaren
     import workloads as wl
 
-    w = wl.WORKLOADS[name]
-    z = w.sizes
     b = Workload()
-    b.name, b.describe = name, w.describe()
-    b.dtype = {"f32": "f32", "bf16": "bf16->f32"}[w.dtype]
+    b.name = name
+    if name != "copy":
+        w = wl.WORKLOADS[name]
+        z = w.sizes
+        b.describe = w.describe()
+        b.dtype = {"f32": "f32", "bf16": "bf16->f32"}[w.dtype]
+
+    if name == "copy":
+        # a plain device copy of known size (the dense batch's K): the practical
+        # read+write ceiling, and the reference the HBM counters are scaled by
+        x = torch.randn(32, 8, 4096, 64, device=device)
+        y = torch.empty_like(x)
+        b.step = lambda: y.copy_(x)
+        b.kind = "copy"
+        b.unit = "bytes/s"
+        b.units = 2 * x.numel() * 4
+        b.bytes_per_launch = 2 * x.numel() * 4
+        b.config = {"workload": "plain device copy, 268,435,456 B read + 268,435,456 B written"}
+        b.kernel = "torch elementwise copy"
+        b.dtype = "f32"
+        b.describe = "copy"
+        b.cpu = None
+        return b
 
     if w.kind == "dense":
         B, H, N, d = z["B"], z["H"], z["N"], z["d"]
@@ -169,7 +188,9 @@ def make(name: str, device):
         b.kind = "step"
         b.units = S * H * T
         b.launches_per_step = T
-        b.bytes_per_launch = S * H * (4 * d * 4 + 4 * 4)  # k,v,w read + w,o written; m,u r/w
+        # per stream-head and append: k, v, w read; w, o written (5 x d x 4 B);
+        # m, u read and written (16 B)
+        b.bytes_per_launch = S * H * (5 * d * 4 + 4 * 4)
         b.config = {"workload": f"RNN step, {T} appends per stream {b.describe}", "S": S, "H": H,
                     "d": d, "appends": T, "in_dtype": "f32", "out_dtype": "f32"}
         b.kernel = "step_kernel"
@@ -227,7 +248,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
-                    choices=["single", "dense", "long_bf16", "ragged", "stream", "reduce"])
+                    choices=["single", "dense", "long_bf16", "ragged", "stream", "reduce",
+                             "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle time budget for cpu_baseline (0 to skip)")
     args = ap.parse_args()
@@ -256,10 +278,10 @@ def main():
     value = b.units / (ms / 1e3)
     launch_s = ms / 1e3 / b.launches_per_step
     achieved = b.bytes_per_launch / launch_s / 1e9
-    traffic = measured_traffic(b.kind, args.workload)
+    traffic = measured_traffic(b.kind, args.workload) if b.kind != "copy" else None
 
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and b.cpu is not None:
         import oracle
         rate, sample = b.cpu(args.cpu_seconds)
         cores = oracle.threads() if args.workload != "reduce" else 1
