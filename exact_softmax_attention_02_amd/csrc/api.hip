@@ -116,6 +116,12 @@ int64_t ceil_div(int64_t a, int64_t b)
     return (a + b - 1) / b;
 }
 
+// Consecutive workgroups per stream (see scan.hip). Measured on MI355X with
+// inputs beyond the Infinity Cache: packed batches fastest at 8 (one per XCD:
+// the heads of a token range are adjacent in memory), dense batches at 2-4.
+constexpr uint32_t kGroupDense = 4;
+constexpr uint32_t kGroupPacked = 8;
+
 // The ticket counters sit right after the header and their number depends on
 // the call's shape; a call's tile slots start where its counters end. Each
 // call leaves its own counters at zero, but its slots may cover bytes that a
@@ -215,7 +221,8 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
     const int rows = aaren::scan_rows_per_tile((int)d, in_dtype);
     const int64_t chunks = ceil_div(N, rows);
     const int64_t tiles = B * H * chunks;
-    if (tiles >= 0x7fffffff)
+    const int64_t chunks_padded = ceil_div(chunks, kGroupDense) * kGroupDense;
+    if (B * H * chunks_padded >= 0x7fffffff)
         return fail(AAREN_ERR_UNSUPPORTED, "%lld tiles exceed the 2^31-1 launch limit",
                     (long long)tiles);
     const size_t need = scan_workspace_bytes(B * H, tiles, 0, d);
@@ -238,6 +245,8 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
     p.stream_stride = N * d;
     p.row_stride = d;
     p.chunks = chunks;
+    p.group = kGroupDense;
+    p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
     p.epoch = next_epoch();
     p.qscale = scale * 1.44269504088896340736f;
@@ -296,7 +305,8 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
     const int rows = aaren::scan_rows_per_tile((int)d, in_dtype);
     const int64_t chunks = ceil_div(total_tokens, rows);
     const int64_t tiles = H * chunks;
-    if (tiles >= 0x7fffffff)
+    const int64_t chunks_padded = ceil_div(chunks, kGroupPacked) * kGroupPacked;
+    if (H * chunks_padded >= 0x7fffffff)
         return fail(AAREN_ERR_UNSUPPORTED, "%lld tiles exceed the 2^31-1 launch limit",
                     (long long)tiles);
     const int64_t words = ceil_div(total_tokens, 32);
@@ -322,6 +332,8 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
     p.stream_stride = d;
     p.row_stride = H * d;
     p.chunks = chunks;
+    p.group = kGroupPacked;
+    p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
     p.epoch = next_epoch();
     p.qscale = scale * 1.44269504088896340736f;

@@ -51,6 +51,14 @@ __device__ __forceinline__ void store16(void *p, u32x4 v)
     *reinterpret_cast<u32x4 *>(p) = v;
 }
 
+// Streaming write of results nobody re-reads in this call: non-temporal.
+// Measured with inputs rotated beyond the 256 MB Infinity Cache: dense batch
+// 143 -> 135 us, packed batch 17.1 -> 16.3 ms per call.
+__device__ __forceinline__ void store16_stream(void *p, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+
 // Widen one 16-byte chunk into E floats (bf16 -> fp32 is exact).
 template <typename T>
 __device__ __forceinline__ void widen(u32x4 raw, float *out);
@@ -82,7 +90,7 @@ __device__ __forceinline__ uint32_t bf16_bits(float f)
     return (x + 0x7fffu + ((x >> 16) & 1u)) >> 16;
 }
 
-// Store E consecutive floats of a row as Tout (E = 4 or 8).
+// Store E consecutive floats of a row as Tout (E = 4 or 8), streaming.
 template <typename Tout, int E>
 __device__ __forceinline__ void store_row(Tout *dst, const float *x)
 {
@@ -91,7 +99,7 @@ __device__ __forceinline__ void store_row(Tout *dst, const float *x)
         for (int c = 0; c < E / 4; ++c) {
             u32x4 v = {__float_as_uint(x[4 * c]), __float_as_uint(x[4 * c + 1]),
                        __float_as_uint(x[4 * c + 2]), __float_as_uint(x[4 * c + 3])};
-            store16(reinterpret_cast<float *>(dst) + 4 * c, v);
+            store16_stream(reinterpret_cast<float *>(dst) + 4 * c, v);
         }
     } else {
         uint32_t w[E / 2];
@@ -100,11 +108,11 @@ __device__ __forceinline__ void store_row(Tout *dst, const float *x)
             w[i] = bf16_bits(x[2 * i]) | (bf16_bits(x[2 * i + 1]) << 16);
         if constexpr (E == 8) {
             u32x4 v = {w[0], w[1], w[2], w[3]};
-            store16(dst, v);
+            store16_stream(dst, v);
         } else {
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             u32x2 v = {w[0], w[1]};
-            *reinterpret_cast<u32x2 *>(dst) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(dst));
         }
     }
 }

@@ -71,7 +71,9 @@ struct ScanParams {
     int64_t stream_stride;   // elements between stream bases: N*d or d
     int64_t row_stride;      // elements between rows of a stream: d or H*d
     int64_t chunks;          // tiles per stream
-    uint32_t num_tiles;
+    uint32_t group;          // consecutive workgroups that serve one stream
+    uint32_t chunks_padded;  // chunks rounded up to a multiple of group
+    uint32_t num_tiles;      // streams * chunks (real tiles)
     uint32_t epoch;          // unique to this call (1 .. 2^31-2)
     float qscale;            // scale * log2(e)
     uint32_t *header;
@@ -108,7 +110,7 @@ struct ReduceParams {
     float qscale;         // scale * log2(e)
 };
 
-constexpr int kReduceMaxParts = 1024;
+constexpr int kReduceMaxParts = 512;
 
 // Launchers (each validates nothing: the API layer did).
 hipError_t launch_scan(const ScanParams &p, int D, aaren_dtype in, aaren_dtype out, bool segmented,

@@ -144,57 +144,56 @@ __global__ __launch_bounds__(64 * WAVES) void reduce_partial_kernel(const Reduce
     }
 }
 
-// One workgroup per (b,h): o = (sum_p f_p w_p) / (sum_p f_p u_p), f_p = 2^(m_p - M).
+// One workgroup of 1024 threads per (b,h): o = (sum_p f_p w_p) / (sum_p f_p u_p)
+// with f_p = 2^(m_p - M), M the largest partial maximum. The partials (at most
+// kReduceMaxParts of them) were just written; every thread issues its loads
+// independently so that one workgroup drains them in a few load latencies.
+constexpr int kFinalThreads = 1024;
+
+__device__ __forceinline__ float block_reduce(float x, float *sh, bool is_max)
+{
+    // wave-level butterfly, then the 16 wave results through LDS
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float y = __shfl_xor(x, off);
+        x = is_max ? fmaxf(x, y) : x + y;
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __syncthreads();
+    if (lane == 0)
+        sh[wave] = x;
+    __syncthreads();
+    float r = sh[0];
+    for (int i = 1; i < kFinalThreads / 64; ++i)
+        r = is_max ? fmaxf(r, sh[i]) : r + sh[i];
+    return r;
+}
+
 template <int D, typename Tout>
-__global__ __launch_bounds__(256) void reduce_final_kernel(const ReduceParams p)
+__global__ __launch_bounds__(kFinalThreads) void reduce_final_kernel(const ReduceParams p)
 {
     constexpr int SLOT = slot_words(D);
-    constexpr int SUB = 256 / D;  // partial subsets per column
+    constexpr int SUB = kFinalThreads / D;  // partial subsets per column
     __shared__ float sh_f[kReduceMaxParts];
-    __shared__ float sh_red[256];
+    __shared__ float sh_red[kFinalThreads / 64];
     __shared__ float sh_col[SUB][D];
-    __shared__ float sh_M, sh_U;
 
     const int tid = threadIdx.x;
     const int64_t unit = blockIdx.x;
     const float *base = p.partials + (size_t)unit * p.parts * SLOT;
-    const int P = (int)p.parts;
+    const int P = (int)p.parts;  // <= kReduceMaxParts <= kFinalThreads
 
-    float mx = kNegInf;
-    for (int i = tid; i < P; i += 256)
-        mx = fmaxf(mx, base[(size_t)i * SLOT]);
-    sh_red[tid] = mx;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s)
-            sh_red[tid] = fmaxf(sh_red[tid], sh_red[tid + s]);
-        __syncthreads();
-    }
-    if (tid == 0)
-        sh_M = sh_red[0];
-    __syncthreads();
-    const float M = sh_M;
-
-    float uu = 0.f;
-    for (int i = tid; i < P; i += 256) {
-        const float mi = base[(size_t)i * SLOT];
-        const float f = (mi == kNegInf) ? 0.f : exp2_fast(mi - M);
-        sh_f[i] = f;
-        uu += f * base[(size_t)i * SLOT + 1];
-    }
-    sh_red[tid] = uu;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s)
-            sh_red[tid] += sh_red[tid + s];
-        __syncthreads();
-    }
-    if (tid == 0)
-        sh_U = sh_red[0];
-    __syncthreads();
+    const float mi = tid < P ? base[(size_t)tid * SLOT] : kNegInf;
+    const float ui = tid < P ? base[(size_t)tid * SLOT + 1] : 0.f;
+    const float M = block_reduce(mi, sh_red, true);
+    const float f = (mi == kNegInf) ? 0.f : exp2_fast(mi - M);
+    if (tid < P)
+        sh_f[tid] = f;
+    const float U = block_reduce(f * ui, sh_red, false);  // syncs: sh_f is visible after
 
     const int col = tid % D, sub = tid / D;
     float acc = 0.f;
+#pragma unroll 16
     for (int i = sub; i < P; i += SUB)
         acc = __builtin_fmaf(sh_f[i], base[(size_t)i * SLOT + 2 + col], acc);
     sh_col[sub][col] = acc;
@@ -204,7 +203,7 @@ __global__ __launch_bounds__(256) void reduce_final_kernel(const ReduceParams p)
 #pragma unroll
         for (int s = 0; s < SUB; ++s)
             w += sh_col[s][tid];
-        const float val = w * rcp_fast(sh_U);
+        const float val = w * rcp_fast(U);
         Tout *o = static_cast<Tout *>(p.o) + unit * D;
         if constexpr (sizeof(Tout) == 4)
             reinterpret_cast<float *>(o)[tid] = val;
@@ -215,13 +214,13 @@ __global__ __launch_bounds__(256) void reduce_final_kernel(const ReduceParams p)
         if (p.m_out)
             p.m_out[unit] = M * kLn2;
         if (p.u_out)
-            p.u_out[unit] = sh_U;
+            p.u_out[unit] = U;
     }
 }
 
 template <int D, typename Tin>
 struct ReduceConfig {
-    static constexpr int R = 8, WAVES = 4;
+    static constexpr int R = 8, WAVES = 8;
 };
 
 template <int D, typename Tin, typename Tout>
@@ -233,8 +232,8 @@ static hipError_t reduce_one(const ReduceParams &p, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((reduce_final_kernel<D, Tout>), dim3((unsigned)p.units), dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((reduce_final_kernel<D, Tout>), dim3((unsigned)p.units),
+                       dim3(kFinalThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -255,13 +254,17 @@ hipError_t launch_reduce(const ReduceParams &p, int D, aaren_dtype in, aaren_dty
     return D == 64 ? reduce_dtypes<64>(p, in, out, stream) : reduce_dtypes<128>(p, in, out, stream);
 }
 
+template <int D, typename Tin>
+static int rows_per_iteration()
+{
+    return ReduceShape<D, Tin, ReduceConfig<D, Tin>::R, ReduceConfig<D, Tin>::WAVES>::ROWS;
+}
+
 int reduce_rows_per_iteration(int D, aaren_dtype in)
 {
     if (D == 64)
-        return in == AAREN_F32 ? ReduceShape<64, float, 8, 4>::ROWS
-                               : ReduceShape<64, bf16, 8, 4>::ROWS;
-    return in == AAREN_F32 ? ReduceShape<128, float, 8, 4>::ROWS
-                           : ReduceShape<128, bf16, 8, 4>::ROWS;
+        return in == AAREN_F32 ? rows_per_iteration<64, float>() : rows_per_iteration<64, bf16>();
+    return in == AAREN_F32 ? rows_per_iteration<128, float>() : rows_per_iteration<128, bf16>();
 }
 
 }  // namespace aaren

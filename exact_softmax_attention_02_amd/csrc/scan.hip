@@ -101,17 +101,22 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     const int gl = lane % L;                     // lane within its group
     const int grp = wave * GPW + lane / L;       // group within the tile
 
-    // Workgroup b works on stream b % streams and draws its position along the
-    // stream from that stream's counter, so a tile only ever waits for tiles
-    // whose workgroups already run (no reliance on dispatch order).
-    const uint32_t stream32 = blockIdx.x % (uint32_t)p.streams;
+    // Workgroups b = g*G .. g*G+G-1 serve stream g % streams (G = p.group) and
+    // draw their positions along the stream from that stream's counter, so a
+    // tile only ever waits for tiles whose workgroups already run (no reliance
+    // on dispatch order). Consecutive workgroups go to different XCDs, so with
+    // G = 8 each XCD sweeps every stream at one chunk offset: for packed
+    // batches the heads of one token range, which are adjacent in memory,
+    // are then read by one XCD at about the same time.
+    const uint32_t stream32 = (blockIdx.x / p.group) % (uint32_t)p.streams;
     if (tid == 0)
         sh_chunk = __builtin_amdgcn_atomic_inc32(p.counters + (size_t)stream32 * kCounterStride,
-                                                 (uint32_t)(p.chunks - 1), __ATOMIC_RELAXED,
-                                                 "agent");
+                                                 p.chunks_padded - 1u, __ATOMIC_RELAXED, "agent");
     __syncthreads();
     const uint32_t chunk32 = __builtin_amdgcn_readfirstlane(sh_chunk);
     const uint32_t epoch = p.epoch;
+    if (chunk32 >= (uint32_t)p.chunks && chunk32 < p.chunks_padded)
+        return;  // a padding position past the end of the stream: nothing to do
     if (chunk32 >= (uint32_t)p.chunks) {  // counter not at zero: refuse to run
         if (tid == 0)
             __hip_atomic_fetch_or(p.header + kError, 1u, __ATOMIC_RELAXED,
@@ -133,11 +138,13 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     for (int r = 0; r < R; ++r) {
         kr[r] = u32x4{0, 0, 0, 0};
         vr[r] = u32x4{0, 0, 0, 0};
-        if (r < nvalid) {
+        if (r < nvalid)
             kr[r] = load16_stream(kp + r * p.row_stride);
-            vr[r] = load16_stream(vp + r * p.row_stride);
-        }
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r)  // keys first: the scores need them first
+        if (r < nvalid)
+            vr[r] = load16_stream(vp + r * p.row_stride);
 
     uint32_t flags = 0;  // bit r: row r of this group starts a sequence
     if constexpr (SEG) {
@@ -451,7 +458,8 @@ static hipError_t launch_one(const ScanParams &p, hipStream_t stream)
     constexpr int R = 16, WAVES = 4;
     static_assert(ScanShape<D, Tin, R, WAVES>::ROWS == scan_tile_rows(D, sizeof(Tin)),
                   "tile rows disagree with the workspace sizing");
-    hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, SEG>), dim3(p.num_tiles),
+    hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, SEG>),
+                       dim3((unsigned)(p.streams * p.chunks_padded)),
                        dim3(64 * WAVES), 0, stream, p);
     return hipGetLastError();
 }

@@ -55,7 +55,7 @@ def test_workspace_sizes():
     assert aaren.aaren_scan_workspace_size(1, 1, 10, 63) == 0
     seg = aaren.aaren_scan_segmented_workspace_size(3, 1000, 8, 64)
     assert seg == 256 + 1024 + 256 + 8 * 4 * 2 * 72 * 8
-    assert aaren.aaren_reduce_workspace_size(1, 1, 1 << 20, 128) == 1024 * 136 * 4
+    assert aaren.aaren_reduce_workspace_size(1, 1, 1 << 20, 128) == 512 * 136 * 4
 
 
 L = aaren.lib
