@@ -90,38 +90,81 @@ __device__ __forceinline__ uint32_t bf16_bits(float f)
     return (x + 0x7fffu + ((x >> 16) & 1u)) >> 16;
 }
 
-// Store E consecutive floats of a row as Tout (E = 4 or 8), streaming.
-template <typename Tout, int E>
-__device__ __forceinline__ void store_row(Tout *dst, const float *x)
+// The columns a lane owns in a row of D elements: its E elements form E/4
+// chunks of 4 consecutive columns, chunk c starting at column
+// c * (D / (E/4)) + 4 * gl (gl = lane within its group). One wave-wide access
+// of a chunk then covers a contiguous run of every row it touches, for loads
+// (16 bytes of fp32 or 2 x 8 bytes of bf16 per lane) and for fp32 or bf16
+// stores alike, so no store leaves a partial cache line behind.
+template <int D, typename Tin>
+struct Slice {
+    static constexpr int E = RowGeo<D, Tin>::kElems;
+    static constexpr int NC = E / 4;      // chunks per lane
+    static constexpr int STRIDE = D / NC; // columns between chunks
+    __device__ static constexpr int col(int gl, int e)
+    {
+        return (e / 4) * STRIDE + 4 * gl + (e % 4);
+    }
+};
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// The lane's 16-byte slice of a row (row points at column 0), raw bits; chunk
+// c occupies words 2c..2c+1 (bf16) or all four words (fp32).
+template <int D, typename Tin, bool STREAM>
+__device__ __forceinline__ u32x4 load_slice(const Tin *row, int gl)
 {
-    if constexpr (sizeof(Tout) == 4) {
+    if constexpr (sizeof(Tin) == 4) {
+        return STREAM ? load16_stream(row + 4 * gl) : load16(row + 4 * gl);
+    } else {
+        const u32x2 *a = reinterpret_cast<const u32x2 *>(row + 4 * gl);
+        const u32x2 *b = reinterpret_cast<const u32x2 *>(row + D / 2 + 4 * gl);
+        const u32x2 x = STREAM ? __builtin_nontemporal_load(a) : *a;
+        const u32x2 y = STREAM ? __builtin_nontemporal_load(b) : *b;
+        return u32x4{x[0], x[1], y[0], y[1]};
+    }
+}
+
+// Store the lane's E floats of a row as Tout (row points at column 0), streaming.
+template <int D, typename Tin, typename Tout>
+__device__ __forceinline__ void store_slice(Tout *row, int gl, const float *x)
+{
+    using S = Slice<D, Tin>;
 #pragma unroll
-        for (int c = 0; c < E / 4; ++c) {
+    for (int c = 0; c < S::NC; ++c) {
+        Tout *dst = row + c * S::STRIDE + 4 * gl;
+        if constexpr (sizeof(Tout) == 4) {
             u32x4 v = {__float_as_uint(x[4 * c]), __float_as_uint(x[4 * c + 1]),
                        __float_as_uint(x[4 * c + 2]), __float_as_uint(x[4 * c + 3])};
-            store16_stream(reinterpret_cast<float *>(dst) + 4 * c, v);
-        }
-    } else {
-        uint32_t w[E / 2];
-#pragma unroll
-        for (int i = 0; i < E / 2; ++i)
-            w[i] = bf16_bits(x[2 * i]) | (bf16_bits(x[2 * i + 1]) << 16);
-        if constexpr (E == 8) {
-            u32x4 v = {w[0], w[1], w[2], w[3]};
             store16_stream(dst, v);
         } else {
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            u32x2 v = {w[0], w[1]};
+            u32x2 v = {bf16_bits(x[4 * c]) | (bf16_bits(x[4 * c + 1]) << 16),
+                       bf16_bits(x[4 * c + 2]) | (bf16_bits(x[4 * c + 3]) << 16)};
             __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(dst));
         }
     }
 }
 
-// Load E consecutive floats of q (any Tin) from a 16-byte aligned row offset.
-template <typename Tin, int E>
-__device__ __forceinline__ void load_query(const Tin *q, float *out)
+// The lane's E fp32 state columns of a row (row points at column 0).
+template <int D, typename Tin>
+__device__ __forceinline__ void load_state(const float *row, int gl, float *x)
 {
-    widen<Tin>(load16(q), out);
+    using S = Slice<D, Tin>;
+#pragma unroll
+    for (int c = 0; c < S::NC; ++c)
+        widen<float>(load16(row + c * S::STRIDE + 4 * gl), x + 4 * c);
+}
+
+template <int D, typename Tin>
+__device__ __forceinline__ void store_state(float *row, int gl, const float *x)
+{
+    using S = Slice<D, Tin>;
+#pragma unroll
+    for (int c = 0; c < S::NC; ++c) {
+        u32x4 v = {__float_as_uint(x[4 * c]), __float_as_uint(x[4 * c + 1]),
+                   __float_as_uint(x[4 * c + 2]), __float_as_uint(x[4 * c + 3])};
+        store16(row + c * S::STRIDE + 4 * gl, v);
+    }
 }
 
 // x + (x from the lane selected by the DPP control); the whole wave is active.

@@ -44,14 +44,15 @@ __global__ __launch_bounds__(64 * WAVES) void reduce_partial_kernel(const Reduce
     int64_t end = begin + p.rows_per_part;
     end = end < p.N ? end : p.N;
 
+    using SL = Slice<D, Tin>;
     float qv[E];
-    load_query<Tin, E>(static_cast<const Tin *>(p.q) + (unit % p.H) * D + gl * E, qv);
+    widen<Tin>(load_slice<D, Tin, false>(static_cast<const Tin *>(p.q) + (unit % p.H) * D, gl), qv);
 #pragma unroll
     for (int e = 0; e < E; ++e)
         qv[e] *= p.qscale;
 
-    const Tin *kb = static_cast<const Tin *>(p.k) + unit * p.N * D + gl * E;
-    const Tin *vb = static_cast<const Tin *>(p.v) + unit * p.N * D + gl * E;
+    const Tin *kb = static_cast<const Tin *>(p.k) + unit * p.N * D;  // column 0
+    const Tin *vb = static_cast<const Tin *>(p.v) + unit * p.N * D;
 
     float gm = kNegInf, gu = 0.f, gw[E];
 #pragma unroll
@@ -68,8 +69,8 @@ __global__ __launch_bounds__(64 * WAVES) void reduce_partial_kernel(const Reduce
             kr[r] = u32x4{0, 0, 0, 0};
             vr[r] = u32x4{0, 0, 0, 0};
             if (r < nvalid) {
-                kr[r] = load16_stream(kb + (row0 + r) * D);
-                vr[r] = load16_stream(vb + (row0 + r) * D);
+                kr[r] = load_slice<D, Tin, true>(kb + (row0 + r) * D, gl);
+                vr[r] = load_slice<D, Tin, true>(vb + (row0 + r) * D, gl);
             }
         }
         float s[R];
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(64 * WAVES) void reduce_partial_kernel(const Reduce
 
 #pragma unroll
     for (int e = 0; e < E; ++e)
-        sh_w[grp][gl * E + e] = gw[e];
+        sh_w[grp][SL::col(gl, e)] = gw[e];
     if (gl == 0) {
         sh_m[grp] = gm;
         sh_u[grp] = gu;

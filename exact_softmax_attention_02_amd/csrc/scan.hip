@@ -11,9 +11,9 @@
 //
 // Design (one HBM pass over K and V, one over O):
 //  * A tile is ROWS consecutive rows of one stream (a (b,h) sequence, or one
-//    head of a packed batch). A lane group of L lanes reads one 16-byte slice
-//    of R consecutive rows per lane, so every wave-wide load is four (or
-//    more) fully used 256-byte row segments.
+//    head of a packed batch). A lane group of L lanes reads a 16-byte slice
+//    of each of R consecutive rows per lane (see Slice in device.h), so every
+//    wave-wide load or store covers whole cache lines.
 //  * Scores: per-lane partial dot products, summed over the group with a DPP
 //    butterfly (no MFMA: the score is a matrix-vector product, bandwidth-bound).
 //  * Pass 1 reduces each group's rows to one state (maximum first, then the
@@ -83,6 +83,7 @@ template <int D, typename Tin, typename Tout, int R, int WAVES, bool SEG>
 __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
 {
     using S = ScanShape<D, Tin, R, WAVES>;
+    using SL = Slice<D, Tin>;
     constexpr int E = S::E, L = S::L, GPW = S::GPW, NG = S::NG, ROWS = S::ROWS;
     constexpr int SLOT = S::SLOT, CPL = S::CPL;
 
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     const int nvalid = left <= 0 ? 0 : (left >= R ? R : (int)left);
 
     // ---- issue every load of the group's rows first --------------------------
-    const int64_t base = stream * p.stream_stride + row0 * p.row_stride + gl * E;
+    const int64_t base = stream * p.stream_stride + row0 * p.row_stride;  // column 0
     const Tin *kp = static_cast<const Tin *>(p.k) + base;
     const Tin *vp = static_cast<const Tin *>(p.v) + base;
     u32x4 kr[R], vr[R];
@@ -139,12 +140,12 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
         kr[r] = u32x4{0, 0, 0, 0};
         vr[r] = u32x4{0, 0, 0, 0};
         if (r < nvalid)
-            kr[r] = load16_stream(kp + r * p.row_stride);
+            kr[r] = load_slice<D, Tin, true>(kp + r * p.row_stride, gl);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)  // keys first: the scores need them first
         if (r < nvalid)
-            vr[r] = load16_stream(vp + r * p.row_stride);
+            vr[r] = load_slice<D, Tin, true>(vp + r * p.row_stride, gl);
 
     uint32_t flags = 0;  // bit r: row r of this group starts a sequence
     if constexpr (SEG) {
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     }
 
     float qv[E];
-    load_query<Tin, E>(static_cast<const Tin *>(p.q) + (stream % p.H) * D + gl * E, qv);
+    widen<Tin>(load_slice<D, Tin, false>(static_cast<const Tin *>(p.q) + (stream % p.H) * D, gl), qv);
 #pragma unroll
     for (int e = 0; e < E; ++e)
         qv[e] *= p.qscale;
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     }
 #pragma unroll
     for (int e = 0; e < E; ++e)
-        sh_gw[grp][gl * E + e] = gwv[e];
+        sh_gw[grp][SL::col(gl, e)] = gwv[e];
     if (gl == 0) {
         sh_gm[grp] = gm;
         sh_gu[grp] = gu;
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
             xu = __builtin_fmaf(fa, xu, fb * bu);
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                xw[e] = __builtin_fmaf(fa, xw[e], fb * sh_gw[g][gl * E + e]);
+                xw[e] = __builtin_fmaf(fa, xw[e], fb * sh_gw[g][SL::col(gl, e)]);
             xm = m;
             xf = xf || bf;
         }
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
         float cw[E];
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            cw[e] = sh_cw[gl * E + e];
+            cw[e] = sh_cw[SL::col(gl, e)];
         combine<E>(sh_cm, sh_cu, cw, pm, pu, pw, xm, xu, xw);
     }
 
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
                 ov[e] = xw[e] * inv;
             }
             xm = hi;
-            store_row<Tout, E>(op + r * p.row_stride, ov);
+            store_slice<D, Tin, Tout>(op + r * p.row_stride, gl, ov);
         }
     }
 

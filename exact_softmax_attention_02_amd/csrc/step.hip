@@ -24,14 +24,12 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p)
     const int64_t h = unit % p.H;
 
     float qv[E], kf[E], vf[E], wv[E];
-    load_query<Tin, E>(static_cast<const Tin *>(p.q) + h * D + gl * E, qv);
-    const int64_t off = unit * D + gl * E;
-    widen<Tin>(load16_stream(static_cast<const Tin *>(p.k) + off), kf);
-    widen<Tin>(load16_stream(static_cast<const Tin *>(p.v) + off), vf);
+    widen<Tin>(load_slice<D, Tin, false>(static_cast<const Tin *>(p.q) + h * D, gl), qv);
+    const int64_t off = unit * D;  // column 0 of this (stream, head)
+    widen<Tin>(load_slice<D, Tin, true>(static_cast<const Tin *>(p.k) + off, gl), kf);
+    widen<Tin>(load_slice<D, Tin, true>(static_cast<const Tin *>(p.v) + off, gl), vf);
     float *wp = p.w + off;
-#pragma unroll
-    for (int c = 0; c < E / 4; ++c)
-        widen<float>(load16(wp + 4 * c), wv + 4 * c);
+    load_state<D, Tin>(wp, gl, wv);
     const float m = p.m[unit], u = p.u[unit];
 
     float part = 0.f;
@@ -52,12 +50,7 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p)
 #pragma unroll
     for (int e = 0; e < E; ++e)
         wv[e] = __builtin_fmaf(wv[e], a, pr * vf[e]);
-#pragma unroll
-    for (int c = 0; c < E / 4; ++c) {
-        u32x4 x = {__float_as_uint(wv[4 * c]), __float_as_uint(wv[4 * c + 1]),
-                   __float_as_uint(wv[4 * c + 2]), __float_as_uint(wv[4 * c + 3])};
-        store16(wp + 4 * c, x);
-    }
+    store_state<D, Tin>(wp, gl, wv);
     if (gl == 0) {
         p.m[unit] = hi;
         p.u[unit] = nu;
@@ -68,7 +61,7 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p)
 #pragma unroll
         for (int e = 0; e < E; ++e)
             ov[e] = wv[e] * inv;
-        store_row<Tout, E>(static_cast<Tout *>(p.o) + off, ov);
+        store_slice<D, Tin, Tout>(static_cast<Tout *>(p.o) + off, gl, ov);
     }
 }
 
