@@ -54,9 +54,9 @@ def _load():
         "aaren_last_error": (ctypes.c_char_p, []),
         "aaren_workspace_clear": (I, [P, SZ, P]),
         "aaren_scan_workspace_size": (SZ, [I64, I64, I64, I64]),
-        "aaren_scan": (I, [P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
+        "aaren_scan": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
         "aaren_scan_segmented_workspace_size": (SZ, [I64, I64, I64, I64]),
-        "aaren_scan_segmented": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
+        "aaren_scan_segmented": (I, [P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
         "aaren_state_init": (I, [P, P, P, I64, I64, I64, P]),
         "aaren_step": (I, [P, P, P, P, P, P, P, I64, I64, I64, F, I, I, P]),
         "aaren_reduce_workspace_size": (SZ, [I64, I64, I64, I64]),
@@ -167,9 +167,11 @@ def aaren_workspace_clear(workspace: torch.Tensor):
                                      _stream(dev)))
 
 
-def aaren_scan(q, k, v, scale=None, out_dtype=None, out=None, workspace=None):
-    """Many-to-many output. q [H,d], k,v [B,H,N,d] -> o [B,H,N,d]."""
-    dev = _need_cuda(q, k, v, out, workspace)
+def aaren_scan(q, k, v, scale=None, out_dtype=None, out=None, workspace=None, lse=None,
+               return_lse=False):
+    """Many-to-many output. q [H,d], k,v [B,H,N,d] -> o [B,H,N,d] (and, with
+    return_lse or a given lse tensor, the log-normaliser [B,H,N] float32)."""
+    dev = _need_cuda(q, k, v, out, workspace, lse)
     B, H, N, d = k.shape
     if q.shape != (H, d) or v.shape != k.shape or q.dtype != k.dtype or v.dtype != k.dtype:
         raise ValueError("expected q [H,d] and k, v [B,H,N,d] of one dtype")
@@ -178,20 +180,24 @@ def aaren_scan(q, k, v, scale=None, out_dtype=None, out=None, workspace=None):
         out = torch.empty(B, H, N, d, dtype=out_dtype, device=dev)
     elif out.shape != k.shape or out.dtype != out_dtype:
         raise ValueError("out must be [B,H,N,d] of out_dtype")
+    if return_lse and lse is None:
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
     need = aaren_scan_workspace_size(B, H, N, d)
     ws = workspace if workspace is not None else _workspace("scan", need, dev, True)
-    _check(lib.aaren_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d,
+    _check(lib.aaren_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                           default_scale(d) if scale is None else float(scale),
                           _dtype_code(k.dtype), _dtype_code(out_dtype),
                           _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                           _stream(dev)))
-    return out
+    return (out, lse) if (return_lse or lse is not None) else out
 
 
-def aaren_scan_segmented(q, k, v, offsets, scale=None, out_dtype=None, out=None, workspace=None):
+def aaren_scan_segmented(q, k, v, offsets, scale=None, out_dtype=None, out=None, workspace=None,
+                         lse=None, return_lse=False):
     """Each packed sequence scanned on its own. q [H,d], k,v [T,H,d],
-    offsets int64 [num_seqs+1] on the device -> o [T,H,d]."""
-    dev = _need_cuda(q, k, v, offsets, out, workspace)
+    offsets int64 [num_seqs+1] on the device -> o [T,H,d] (and, with
+    return_lse or a given lse tensor, the log-normaliser [T,H] float32)."""
+    dev = _need_cuda(q, k, v, offsets, out, workspace, lse)
     T, H, d = k.shape
     if q.shape != (H, d) or v.shape != k.shape or q.dtype != k.dtype or v.dtype != k.dtype:
         raise ValueError("expected q [H,d] and k, v [T,H,d] of one dtype")
@@ -203,14 +209,17 @@ def aaren_scan_segmented(q, k, v, offsets, scale=None, out_dtype=None, out=None,
         out = torch.empty(T, H, d, dtype=out_dtype, device=dev)
     elif out.shape != k.shape or out.dtype != out_dtype:
         raise ValueError("out must be [T,H,d] of out_dtype")
+    if return_lse and lse is None:
+        lse = torch.empty(T, H, dtype=torch.float32, device=dev)
     need = aaren_scan_segmented_workspace_size(S, T, H, d)
     ws = workspace if workspace is not None else _workspace("scan", need, dev, True)
-    _check(lib.aaren_scan_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(offsets), S, T, H,
+    _check(lib.aaren_scan_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                    _ptr(offsets), S, T, H,
                                     d, default_scale(d) if scale is None else float(scale),
                                     _dtype_code(k.dtype), _dtype_code(out_dtype), _ptr(ws),
                                     0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(dev)))
-    return out
+    return (out, lse) if (return_lse or lse is not None) else out
 
 
 def aaren_state_init(m, u, w):

@@ -200,8 +200,8 @@ AAREN_API size_t aaren_scan_workspace_size(int64_t B, int64_t H, int64_t N, int6
     return scan_workspace_bytes(B * H, tiles, 0, d);
 }
 
-AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, int64_t B,
-                                  int64_t H, int64_t N, int64_t d, float scale,
+AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, float *lse,
+                                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                                   aaren_dtype in_dtype, aaren_dtype out_dtype, void *workspace,
                                   size_t workspace_bytes, void *hip_stream)
 {
@@ -218,6 +218,8 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
     CHECK(check_ptr(k, "k"));
     CHECK(check_ptr(v, "v"));
     CHECK(check_ptr(o, "o"));
+    if (reinterpret_cast<uintptr_t>(lse) & 3u)
+        return fail(AAREN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
     const int rows = aaren::scan_rows_per_tile((int)d, in_dtype);
     const int64_t chunks = ceil_div(N, rows);
     const int64_t tiles = B * H * chunks;
@@ -237,6 +239,9 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
     p.k = k;
     p.v = v;
     p.o = o;
+    p.lse = lse;
+    p.lse_stream_stride = N;
+    p.lse_row_stride = 1;
     p.bitmap = nullptr;
     p.bitmap_words = 0;
     p.rows = N;
@@ -277,7 +282,7 @@ AAREN_API size_t aaren_scan_segmented_workspace_size(int64_t num_seqs, int64_t t
 }
 
 AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const void *v, void *o,
-                                            const int64_t *offsets, int64_t num_seqs,
+                                            float *lse, const int64_t *offsets, int64_t num_seqs,
                                             int64_t total_tokens, int64_t H, int64_t d,
                                             float scale, aaren_dtype in_dtype,
                                             aaren_dtype out_dtype, void *workspace,
@@ -298,6 +303,8 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
         return fail(AAREN_ERR_INVALID_ARG, "offsets is NULL");
     if ((reinterpret_cast<uintptr_t>(offsets) & 7u) != 0)
         return fail(AAREN_ERR_ALIGNMENT, "offsets is not 8-byte aligned");
+    if (reinterpret_cast<uintptr_t>(lse) & 3u)
+        return fail(AAREN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
     CHECK(check_ptr(q, "q"));
     CHECK(check_ptr(k, "k"));
     CHECK(check_ptr(v, "v"));
@@ -324,6 +331,9 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
     p.k = k;
     p.v = v;
     p.o = o;
+    p.lse = lse;
+    p.lse_stream_stride = 1;
+    p.lse_row_stride = H;
     p.bitmap = bitmap;
     p.bitmap_words = words;
     p.rows = total_tokens;

@@ -198,6 +198,11 @@ __device__ __forceinline__ float exp2_fast(float x)
     return __builtin_amdgcn_exp2f(x);
 }
 
+__device__ __forceinline__ float log2_fast(float x)
+{
+    return __builtin_amdgcn_logf(x);
+}
+
 __device__ __forceinline__ float rcp_fast(float x)
 {
     return __builtin_amdgcn_rcpf(x);

@@ -63,6 +63,8 @@ struct ScanParams {
     const void *k;
     const void *v;
     void *o;
+    float *lse;              // log-normaliser per row, or null
+    int64_t lse_stream_stride, lse_row_stride;
     const uint32_t *bitmap;  // segment starts, one bit per row (segmented only)
     int64_t bitmap_words;
     int64_t rows;            // rows per stream: N (dense) or T (segmented)

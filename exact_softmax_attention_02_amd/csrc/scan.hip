@@ -387,6 +387,11 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     }
 
     Tout *op = static_cast<Tout *>(p.o) + base;
+    constexpr int LPL = (R + L - 1) / L;  // rows whose log-normaliser a lane stores
+    float my_lse[LPL];
+#pragma unroll
+    for (int j = 0; j < LPL; ++j)
+        my_lse[j] = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         if (r < nvalid) {
@@ -418,6 +423,16 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
             }
             xm = hi;
             store_slice<D, Tin, Tout>(op + r * p.row_stride, gl, ov);
+            if (p.lse && r % L == gl)  // L_k = (m + log2 u) ln 2, natural units
+                my_lse[r / L] = (xm + log2_fast(xu)) * kLn2;
+        }
+    }
+    if (p.lse) {  // lane j of the group writes row j: one contiguous store per group
+#pragma unroll
+        for (int j = 0; j < LPL; ++j) {
+            const int r = j * L + gl;
+            if (r < nvalid)
+                p.lse[stream * p.lse_stream_stride + (row0 + r) * p.lse_row_stride] = my_lse[j];
         }
     }
 

@@ -99,10 +99,12 @@ aaren_status aaren_workspace_clear(void *workspace, size_t workspace_bytes, void
  *   q [H,d], k [B,H,N,d], v [B,H,N,d]  (in_dtype)
  *   o [B,H,N,d]                         (out_dtype), o[b,h,i] = attention of
  *                                       q[h] over pairs 0..i of (b,h)
+ *   lse [B,H,N] float32 or NULL: the log-normaliser L_i = ln sum_{j<=i} e^{s_j}
+ *                                of every row (what aaren_scan_backward needs)
  * B*H*N == 0 is a no-op. Returns WORKSPACE if workspace_bytes is below
  * aaren_scan_workspace_size(B,H,N,d). */
 size_t aaren_scan_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d);
-aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o,
+aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, float *lse,
                         int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                         aaren_dtype in_dtype, aaren_dtype out_dtype,
                         void *workspace, size_t workspace_bytes, void *hip_stream);
@@ -120,6 +122,7 @@ aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o,
 size_t aaren_scan_segmented_workspace_size(int64_t num_seqs, int64_t total_tokens,
                                            int64_t H, int64_t d);
 aaren_status aaren_scan_segmented(const void *q, const void *k, const void *v, void *o,
+                                  float *lse /* [T,H] or NULL */,
                                   const int64_t *offsets, int64_t num_seqs,
                                   int64_t total_tokens, int64_t H, int64_t d, float scale,
                                   aaren_dtype in_dtype, aaren_dtype out_dtype,

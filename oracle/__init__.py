@@ -56,7 +56,10 @@ def _configure(lib):
                                 i64, i64, i64, ctypes.c_double]
     lib.oracle_reduce.argtypes = [f32p, f32p, f32p, i64, i64, i64, i64, ctypes.c_double,
                                   f64p, opt64, opt64]
-    for fn in (lib.oracle_scan, lib.oracle_scan_segmented, lib.oracle_step, lib.oracle_reduce):
+    lib.oracle_scan_backward.argtypes = [f32p, f32p, f32p, f32p, i64, i64, i64, i64,
+                                         ctypes.c_double, f64p, f64p, f64p]
+    for fn in (lib.oracle_scan, lib.oracle_scan_segmented, lib.oracle_step, lib.oracle_reduce,
+               lib.oracle_scan_backward):
         fn.restype = ctypes.c_int
     return lib
 
@@ -148,6 +151,21 @@ def reduce(q, k, v, scale, stats: bool = False):
     if rc:
         raise ValueError("oracle_reduce rejected its arguments")
     return (o, m, lse) if stats else o
+
+
+def scan_backward(q, k, v, dout, scale):
+    """Gradients of the many-to-many output given dout: q [H,d], k, v, dout
+    [B,H,N,d] float32 -> (dq [H,d], dk, dv [B,H,N,d]) float64."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, H, N, d = k.shape
+    assert q.shape == (H, d) and v.shape == k.shape and dout.shape == k.shape
+    dq = np.empty((H, d), np.float64)
+    dk = np.empty((B, H, N, d), np.float64)
+    dv = np.empty((B, H, N, d), np.float64)
+    rc = _load().oracle_scan_backward(q, k, v, dout, B, H, N, d, float(scale), dq, dk, dv)
+    if rc:
+        raise ValueError("oracle_scan_backward rejected its arguments")
+    return dq, dk, dv
 
 
 def max_scaled_err(got, ref) -> float:

@@ -28,6 +28,18 @@
  *  - Packed variable-length batches restart the recurrence at each sequence
  *    start; the per-token RNN update absorbs exactly one pair into a stored
  *    (m, u, w) state; the many-to-one reduction keeps only the last output.
+ *  - Gradients. "Attention as an RNN" (review, proposed method) presents the
+ *    many-to-many form as differentiable and trained in parallel, and the
+ *    memory-efficient-attention review reports differentiation (abstract;
+ *    section 5.2, body lost) without a formula. The gradient used here is
+ *    derived from the definition: with p_ki = e^{s_i - L_k} the weight of
+ *    pair i in output k (L_k = ln sum_{j<=k} e^{s_j}) and g_k = dloss/do_k,
+ *      dv_i = sum_{k>=i} p_ki g_k,
+ *      ds_i = sum_{k>=i} p_ki <g_k, v_i - o_k> = <dv_i, v_i> - sum_{k>=i} p_ki <g_k, o_k>,
+ *      dk_i = scale ds_i q,  dq = scale sum_i ds_i k_i.
+ *    Both suffix sums are evaluated backwards from the last pair, each term
+ *    weighted by e^{L_i - L_k} <= 1 relative to the current position (L is
+ *    non-decreasing along the sequence), then multiplied by p_ii = e^{s_i - L_i}.
  *
  * Notation: m = running maximum score, u = scalar accumulator (sum of
  * e^{s_i - m}), w = vector accumulator (sum of e^{s_i - m} v_i). Inputs arrive
@@ -203,5 +215,78 @@ int oracle_reduce(const float *q, const float *k, const float *v,
         }
         free(w);
     }
+    return 0;
+}
+
+/* Gradients of the many-to-many output for a dense batch, given the output
+ * gradient dout [B,H,N,d]: dq [H,d] (summed over the batch), dk, dv [B,H,N,d].
+ * The forward values o_k and L_k are recomputed here, in double. */
+int oracle_scan_backward(const float *q, const float *k, const float *v, const float *dout,
+                         int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                         double *dq, double *dk, double *dv)
+{
+    if (B < 0 || H < 0 || N < 0 || d < 1)
+        return 1;
+    int64_t units = B * H;
+    double *dq_unit = (double *)calloc((size_t)(units > 0 ? units : 1) * (size_t)d, sizeof(double));
+#pragma omp parallel
+    {
+        double *w = (double *)malloc((size_t)d * sizeof(double));
+        double *o = (double *)malloc((size_t)(N > 0 ? N : 1) * (size_t)d * sizeof(double));
+        double *L = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        double *s = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        double *G = (double *)malloc((size_t)d * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t unit = 0; unit < units; ++unit) {
+            const float *qh = q + (unit % H) * d;
+            /* forward: o_k and L_k */
+            double m = -INFINITY, u = 0.0;
+            memset(w, 0, (size_t)d * sizeof(double));
+            for (int64_t i = 0; i < N; ++i) {
+                int64_t row = unit * N + i;
+                s[i] = score(qh, k + row * d, d, scale);
+                absorb(&m, &u, w, d, s[i], v + row * d);
+                emit(m, u, w, d, o + i * d, NULL, &L[i]);
+            }
+            /* backward: suffix sums G (vector) and D (scalar) relative to e^{-L_i} */
+            double D = 0.0;
+            memset(G, 0, (size_t)d * sizeof(double));
+            for (int64_t i = N - 1; i >= 0; --i) {
+                int64_t row = unit * N + i;
+                const float *g = dout + row * d;
+                double shrink = (i == N - 1) ? 0.0 : exp(L[i] - L[i + 1]);
+                double delta = 0.0;
+                for (int64_t j = 0; j < d; ++j)
+                    delta += (double)g[j] * o[i * d + j];
+                D = delta + shrink * D;
+                for (int64_t j = 0; j < d; ++j)
+                    G[j] = (double)g[j] + shrink * G[j];
+                double pii = exp(s[i] - L[i]);
+                double ds = 0.0;
+                for (int64_t j = 0; j < d; ++j) {
+                    dv[row * d + j] = pii * G[j];
+                    ds += dv[row * d + j] * (double)v[row * d + j];
+                }
+                ds -= pii * D;
+                for (int64_t j = 0; j < d; ++j) {
+                    dk[row * d + j] = scale * ds * (double)qh[j];
+                    dq_unit[unit * d + j] += scale * ds * (double)k[row * d + j];
+                }
+            }
+        }
+        free(w);
+        free(o);
+        free(L);
+        free(s);
+        free(G);
+    }
+    for (int64_t h = 0; h < H; ++h)
+        for (int64_t j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < B; ++b)
+                acc += dq_unit[(b * H + h) * d + j];
+            dq[h * d + j] = acc;
+        }
+    free(dq_unit);
     return 0;
 }

@@ -82,6 +82,44 @@ def softmax_reduce(q, K, V, scale):
     return (w @ Vt).numpy()
 
 
+def brute_scan_grads(q, K, V, G, scale):
+    """Gradients of the many-to-many output of one sequence, written out from
+    the definition: o_k = sum_{i<=k} w_ki v_i with w_k = softmax(s_1..s_k),
+    so do_k/dv_i = w_ki and do_k/ds_i = w_ki (v_i - o_k). G [n,d] holds
+    dloss/do_k. Returns (dq [d], dK [n,d], dV [n,d]). O(n^2 d)."""
+    q = np.asarray(q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    G = np.asarray(G, np.float64)
+    n = K.shape[0]
+    s = scores(q, K, scale)
+    dV = np.zeros_like(V)
+    ds = np.zeros(n)
+    for k in range(n):
+        p = np.exp(s[: k + 1] - s[: k + 1].max())
+        w = p / p.sum()
+        o_k = w @ V[: k + 1]
+        dV[: k + 1] += w[:, None] * G[k][None, :]
+        ds[: k + 1] += w * ((V[: k + 1] - o_k) @ G[k])
+    dK = float(scale) * ds[:, None] * q[None, :]
+    dq = float(scale) * (ds @ K)
+    return dq, dK, dV
+
+
+def autograd_scan_grads(q, K, V, G, scale):
+    """The same gradients from torch autograd through scaled_dot_product_attention
+    (CPU, float64, causal, the query repeated n times)."""
+    import torch
+    qt = torch.tensor(np.asarray(q, np.float64), requires_grad=True)
+    Kt = torch.tensor(np.asarray(K, np.float64), requires_grad=True)
+    Vt = torch.tensor(np.asarray(V, np.float64), requires_grad=True)
+    Q = qt.expand(Kt.shape[0], -1)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        Q[None, None], Kt[None, None], Vt[None, None], is_causal=True, scale=float(scale))[0, 0]
+    out.backward(torch.tensor(np.asarray(G, np.float64)))
+    return qt.grad.numpy(), Kt.grad.numpy(), Vt.grad.numpy()
+
+
 # ---- the combine operator (derived; see module docstring) -------------------
 
 IDENTITY = None  # marker for the empty state

@@ -279,6 +279,84 @@ def check_segmented(orc, seed=21):
     assert np.array_equal(o[one], v[one].astype(np.float64)), "length-1 segment"
 
 
+# --- gradients ---------------------------------------------------------------
+
+def check_backward(orc, seed=22):
+    """The oracle's gradients (reverse recurrence) == the definition written
+    out (brute force) == torch autograd through SDPA, float64, including a
+    spread that takes scores far past the range of exp; dq sums over the batch."""
+    rng = _rng(seed)
+    for (B, H, N, d, spread, scale) in ((2, 2, 40, 6, 1.0, 0.4), (1, 3, 70, 16, 25.0, 2.0),
+                                        (2, 1, 1, 4, 1.0, 1.0)):
+        q = rng.standard_normal((H, d)).astype(np.float32)
+        k = (spread * rng.standard_normal((B, H, N, d))).astype(np.float32)
+        v = rng.standard_normal((B, H, N, d)).astype(np.float32)
+        g = rng.standard_normal((B, H, N, d)).astype(np.float32)
+        dq, dk, dv = orc.scan_backward(q, k, v, g, scale)
+        for h in range(H):
+            acc = np.zeros(d)
+            for b in range(B):
+                bq, bk, bv = brute.brute_scan_grads(q[h], k[b, h], v[b, h], g[b, h], scale)
+                aq, ak, av = brute.autograd_scan_grads(q[h], k[b, h], v[b, h], g[b, h], scale)
+                _close(dk[b, h], bk, 1e-11, "dk vs definition")
+                _close(dv[b, h], bv, 1e-11, "dv vs definition")
+                _close(bk, ak, 1e-11, "dk definition vs autograd")
+                _close(bv, av, 1e-11, "dv definition vs autograd")
+                _close(bq, aq, 1e-11, "dq definition vs autograd")
+                acc += bq
+            _close(dq[h], acc, 1e-11, "dq (batch sum) vs definition")
+
+
+def check_backward_finite_differences(orc, seed=23):
+    """Central differences of loss = sum(g * o) through the forward oracle."""
+    rng = _rng(seed)
+    B, H, N, d, scale = 1, 1, 5, 3, 0.7
+    q = rng.standard_normal((H, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    g = rng.standard_normal((B, H, N, d))
+    dq, dk, dv = orc.scan_backward(*(x.astype(np.float32) for x in (q, k, v, g)), scale)
+    # finite differences need inputs exactly representable in float32
+    q, k, v, g = (x.astype(np.float32).astype(np.float64) for x in (q, k, v, g))
+
+    def loss(q_, k_, v_):
+        o = orc.scan(q_.astype(np.float32), k_.astype(np.float32), v_.astype(np.float32), scale)
+        return float((o * g).sum())
+    h = 2.0 ** -10  # exact in float32 for these magnitudes
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        flat = x.reshape(-1)
+        for i in range(0, flat.size, max(1, flat.size // 7)):
+            old = flat[i]
+            flat[i] = old + h
+            lp = loss(q, k, v)
+            flat[i] = old - h
+            lm = loss(q, k, v)
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad.reshape(-1)[i]) <= 1e-5 * (1 + abs(fd)), (name, i, fd)
+
+
+def check_backward_closed_forms(orc, seed=24):
+    """One pair: o_1 = v_1, so dv_1 = g_1 and the score gradient is 0. Equal
+    scores (q = 0): dv_i = sum_{k>=i} g_k / k."""
+    rng = _rng(seed)
+    q = rng.standard_normal((2, 8)).astype(np.float32)
+    k = rng.standard_normal((3, 2, 1, 8)).astype(np.float32)
+    v = rng.standard_normal((3, 2, 1, 8)).astype(np.float32)
+    g = rng.standard_normal((3, 2, 1, 8)).astype(np.float32)
+    dq, dk, dv = orc.scan_backward(q, k, v, g, 0.3)
+    assert np.array_equal(dv, g.astype(np.float64)), "dv_1 != g_1"
+    assert np.all(np.abs(dk) <= 1e-15) and np.all(np.abs(dq) <= 1e-14), "single pair: ds != 0"
+    N = 50
+    k = rng.standard_normal((1, 1, N, 4)).astype(np.float32)
+    v = rng.standard_normal((1, 1, N, 4)).astype(np.float32)
+    g = rng.standard_normal((1, 1, N, 4)).astype(np.float32)
+    _, _, dv = orc.scan_backward(np.zeros((1, 4), np.float32), k, v, g, 1.0)
+    ref = np.cumsum((g[0, 0].astype(np.float64) / np.arange(1, N + 1)[:, None])[::-1], axis=0)[::-1]
+    _close(dv[0, 0], ref, 1e-13, "equal-score dv")
+
+
 ALL = [check_golden, check_scan_vs_definition, check_stats, check_single_token,
        check_running_mean, check_two_tokens, check_dominating_key, check_shift_invariance,
-       check_convex_hull, check_bracketing, check_reduce, check_step, check_segmented]
+       check_convex_hull, check_bracketing, check_reduce, check_step, check_segmented,
+       check_backward, check_backward_finite_differences, check_backward_closed_forms]

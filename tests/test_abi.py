@@ -63,8 +63,8 @@ A = 0x10000  # an aligned, never-dereferenced address
 S = {"ok": 0, "arg": 1, "unsup": 2, "align": 3, "ws": 4}
 
 
-def scan(q=A, k=A, v=A, o=A, B=1, H=1, N=16, d=64, ind=0, outd=0, ws=A, wsb=1 << 30):
-    return L.aaren_scan(q, k, v, o, B, H, N, d, 0.125, ind, outd, ws, wsb, None)
+def scan(q=A, k=A, v=A, o=A, lse=None, B=1, H=1, N=16, d=64, ind=0, outd=0, ws=A, wsb=1 << 30):
+    return L.aaren_scan(q, k, v, o, lse, B, H, N, d, 0.125, ind, outd, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -72,6 +72,7 @@ def scan(q=A, k=A, v=A, o=A, B=1, H=1, N=16, d=64, ind=0, outd=0, ws=A, wsb=1 <<
     (dict(ind=7), "unsup"), (dict(outd=3), "unsup"), (dict(q=0), "arg"), (dict(k=0), "arg"),
     (dict(o=0), "arg"), (dict(v=A + 8), "align"), (dict(o=A + 4), "align"),
     (dict(ws=0), "ws"), (dict(wsb=100), "ws"), (dict(ws=A + 8), "align"),
+    (dict(lse=A + 2), "align"),
 ])
 def test_scan_validation(kw, status):
     assert scan(**kw) == S[status]
@@ -83,13 +84,14 @@ def test_scan_empty_is_a_noop():
     assert scan(q=0, k=0, v=0, o=0, ws=0, wsb=0, B=0) == 0
 
 
-def seg(offs=A, S_=2, T=10, H=1, d=64, q=A, wsb=1 << 30):
-    return L.aaren_scan_segmented(q, A, A, A, offs, S_, T, H, d, 0.125, 0, 0, A, wsb, None)
+def seg(offs=A, S_=2, T=10, H=1, d=64, q=A, wsb=1 << 30, lse=None):
+    return L.aaren_scan_segmented(q, A, A, A, lse, offs, S_, T, H, d, 0.125, 0, 0, A, wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(offs=0), "arg"), (dict(offs=A + 4), "align"), (dict(S_=-1), "arg"),
     (dict(S_=0, T=5), "arg"), (dict(d=96), "unsup"), (dict(q=A + 2), "align"), (dict(wsb=64), "ws"),
+    (dict(lse=A + 1), "align"),
 ])
 def test_segmented_validation(kw, status):
     assert seg(**kw) == S[status]

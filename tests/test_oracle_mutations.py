@@ -52,6 +52,19 @@ MUTATIONS = [
      "for (int64_t i = 0; i < N - 1; ++i)"),
     ("reduce reads rows of the wrong unit", "oracle_reduce", "int64_t row = unit * N + i;",
      "int64_t row = (unit % H) * N + i;"),
+    ("backward: suffix weight inverted", "oracle_scan_backward", "exp(L[i] - L[i + 1])",
+     "exp(L[i + 1] - L[i])"),
+    ("backward: <g, v> in place of <g, o>", "oracle_scan_backward",
+     "delta += (double)g[j] * o[i * d + j];", "delta += (double)g[j] * (double)v[row * d + j];"),
+    ("backward: dv without the diagonal weight", "oracle_scan_backward",
+     "dv[row * d + j] = pii * G[j];", "dv[row * d + j] = G[j];"),
+    ("backward: score gradient without the output term", "oracle_scan_backward",
+     "ds -= pii * D;", ";"),
+    ("backward: dk along k instead of q", "oracle_scan_backward",
+     "dk[row * d + j] = scale * ds * (double)qh[j];",
+     "dk[row * d + j] = scale * ds * (double)k[row * d + j];"),
+    ("backward: dq of the first batch row only", "oracle_scan_backward",
+     "for (int64_t b = 0; b < B; ++b)", "for (int64_t b = 0; b < 1; ++b)"),
 ]
 
 
