@@ -30,7 +30,7 @@ EXPORTS = (
     "aaren_version", "aaren_status_string", "aaren_last_error", "aaren_workspace_clear",
     "aaren_scan_workspace_size", "aaren_scan", "aaren_scan_segmented_workspace_size",
     "aaren_scan_segmented", "aaren_state_init", "aaren_step", "aaren_reduce_workspace_size",
-    "aaren_reduce",
+    "aaren_reduce", "aaren_scan_backward_workspace_size", "aaren_scan_backward",
 )
 
 
@@ -61,6 +61,8 @@ def _load():
         "aaren_step": (I, [P, P, P, P, P, P, P, I64, I64, I64, F, I, I, P]),
         "aaren_reduce_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_reduce": (I, [P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
+        "aaren_scan_backward_workspace_size": (SZ, [I64, I64, I64, I64]),
+        "aaren_scan_backward": (I, [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -220,6 +222,36 @@ def aaren_scan_segmented(q, k, v, offsets, scale=None, out_dtype=None, out=None,
                                     0 if ws is None else ws.numel() * ws.element_size(),
                                     _stream(dev)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def aaren_scan_backward_workspace_size(B, H, N, d) -> int:
+    return int(lib.aaren_scan_backward_workspace_size(B, H, N, d))
+
+
+def aaren_scan_backward(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None,
+                        workspace=None):
+    """Gradients of the dense many-to-many scan: (dq [H,d], dk, dv [B,H,N,d]),
+    float32, from the forward's o and lse and the output gradient dout."""
+    dev = _need_cuda(q, k, v, o, dout, lse, dq, dk, dv, workspace)
+    B, H, N, d = k.shape
+    for t in (q, k, v, o, dout, lse):
+        if t.dtype != torch.float32:
+            raise TypeError("the backward pass takes float32 tensors")
+    if q.shape != (H, d) or not (v.shape == o.shape == dout.shape == k.shape) or \
+            lse.shape != (B, H, N):
+        raise ValueError("expected q [H,d], k, v, o, dout [B,H,N,d] and lse [B,H,N]")
+    dq = torch.empty(H, d, dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = aaren_scan_backward_workspace_size(B, H, N, d)
+    ws = workspace if workspace is not None else _workspace("scan", need, dev, True)
+    _check(lib.aaren_scan_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+                                   default_scale(d) if scale is None else float(scale),
+                                   AAREN_F32, _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(),
+                                   _stream(dev)))
+    return dq, dk, dv
 
 
 def aaren_state_init(m, u, w):

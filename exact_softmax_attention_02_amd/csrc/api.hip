@@ -268,6 +268,110 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
                       "scan launch");
 }
 
+// ---- backward of the dense scan -----------------------------------------------
+
+namespace {
+
+size_t backward_slots_bytes(int64_t tiles, int64_t d)
+{
+    return (size_t)tiles * 2 * aaren::slot_words((int)d) * 8;
+}
+
+}  // namespace
+
+AAREN_API size_t aaren_scan_backward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d)
+{
+    if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128))
+        return 0;
+    const int64_t tiles = mul_checked({B, H, ceil_div(N, aaren::backward_tile_rows((int)d))});
+    if (tiles < 0)
+        return 0;
+    return aaren::kHeaderBytes + counter_bytes(B * H) + backward_slots_bytes(tiles, d) +
+           aaren::round256((size_t)tiles * d * 4);
+}
+
+AAREN_API aaren_status aaren_scan_backward(const void *q, const void *k, const void *v,
+                                           const void *o, const void *dout, const float *lse,
+                                           float *dq, float *dk, float *dv, int64_t B, int64_t H,
+                                           int64_t N, int64_t d, float scale, aaren_dtype in_dtype,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *hip_stream)
+{
+    if (B < 0 || H < 0 || N < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
+                    (long long)B, (long long)H, (long long)N);
+    CHECK(check_common(d, in_dtype, AAREN_F32));
+    if (in_dtype != AAREN_F32)
+        return fail(AAREN_ERR_UNSUPPORTED, "the backward pass takes float32 tensors");
+    const int64_t elems = mul_checked({B, H, N, d});
+    if (elems < 0 || mul_checked({H, d}) < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "B*H*N*d overflows");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (elems == 0) {  // no rows: dq is an empty sum
+        if (H * d == 0)
+            return AAREN_OK;
+        CHECK(check_ptr(dq, "dq"));
+        return hip_status(aaren::launch_fill_zero(dq, (size_t)(H * d) * 4, st), "dq clear launch");
+    }
+    CHECK(check_ptr(q, "q"));
+    CHECK(check_ptr(k, "k"));
+    CHECK(check_ptr(v, "v"));
+    CHECK(check_ptr(o, "o"));
+    CHECK(check_ptr(dout, "dout"));
+    CHECK(check_ptr(dq, "dq"));
+    CHECK(check_ptr(dk, "dk"));
+    CHECK(check_ptr(dv, "dv"));
+    if (!lse)
+        return fail(AAREN_ERR_INVALID_ARG, "lse is NULL");
+    if (reinterpret_cast<uintptr_t>(lse) & 3u)
+        return fail(AAREN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
+    const int64_t rows = aaren::backward_tile_rows((int)d);
+    const int64_t chunks = ceil_div(N, rows);
+    const int64_t tiles = B * H * chunks;
+    const int64_t chunks_padded = ceil_div(chunks, kGroupDense) * kGroupDense;
+    if (B * H * chunks_padded >= 0x7fffffff)
+        return fail(AAREN_ERR_UNSUPPORTED, "%lld tiles exceed the 2^31-1 launch limit",
+                    (long long)tiles);
+    const size_t need = aaren_scan_backward_workspace_size(B, H, N, d);
+    if (!workspace || workspace_bytes < need)
+        return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    need);
+    if (!aligned16(workspace))
+        return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    aaren::BackwardParams p{};
+    p.q = static_cast<const float *>(q);
+    p.k = static_cast<const float *>(k);
+    p.v = static_cast<const float *>(v);
+    p.o = static_cast<const float *>(o);
+    p.g = static_cast<const float *>(dout);
+    p.lse = lse;
+    p.dk = dk;
+    p.dv = dv;
+    p.dq = dq;
+    p.streams = B * H;
+    p.H = H;
+    p.N = N;
+    p.chunks = chunks;
+    p.group = kGroupDense;
+    p.chunks_padded = (uint32_t)chunks_padded;
+    p.num_tiles = (uint32_t)tiles;
+    p.epoch = next_epoch();
+    p.scale = scale;
+    p.qscale = scale * 1.44269504088896340736f;
+    p.header = reinterpret_cast<uint32_t *>(ws);
+    p.counters = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes);
+    p.slots = reinterpret_cast<uint64_t *>(ws + aaren::kHeaderBytes + counter_bytes(B * H));
+    p.dq_partial = reinterpret_cast<float *>(ws + aaren::kHeaderBytes + counter_bytes(B * H) +
+                                             backward_slots_bytes(tiles, d));
+    if (log_enabled())
+        fprintf(stderr, "[aaren] scan_backward B=%lld H=%lld N=%lld d=%lld tiles=%lld\n",
+                (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles);
+    CHECK(prepare_counters(workspace, counter_bytes(B * H), st));
+    return hip_status(aaren::launch_scan_backward(p, (int)d, st), "scan backward launch");
+}
+
 // ---- segmented scan -------------------------------------------------------------
 
 AAREN_API size_t aaren_scan_segmented_workspace_size(int64_t num_seqs, int64_t total_tokens,

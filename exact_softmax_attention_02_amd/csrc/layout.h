@@ -114,6 +114,39 @@ struct ReduceParams {
 
 constexpr int kReduceMaxParts = 512;
 
+// Rows one backward tile covers: 128 (16 lane groups of 8 rows for d = 64,
+// 16 groups over 8 waves for d = 128); five row tensors are held per lane.
+__host__ __device__ constexpr int backward_tile_rows(int D)
+{
+    return 128 + 0 * D;
+}
+
+struct BackwardParams {
+    const float *q;
+    const float *k;
+    const float *v;
+    const float *o;
+    const float *g;          // dloss/do
+    const float *lse;        // log-normaliser per row, natural units
+    float *dk;
+    float *dv;
+    float *dq_partial;       // [tiles][D], one per tile
+    float *dq;               // [H][D]
+    int64_t streams;         // B*H
+    int64_t H;
+    int64_t N;
+    int64_t chunks;
+    uint32_t group;
+    uint32_t chunks_padded;
+    uint32_t num_tiles;
+    uint32_t epoch;
+    float scale;
+    float qscale;            // scale * log2(e)
+    uint32_t *header;
+    uint32_t *counters;
+    uint64_t *slots;
+};
+
 // Launchers (each validates nothing: the API layer did).
 hipError_t launch_scan(const ScanParams &p, int D, aaren_dtype in, aaren_dtype out, bool segmented,
                        hipStream_t stream);
@@ -128,5 +161,6 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams &p, int D, aaren_dtype in, aaren_dtype out,
                          hipStream_t stream);
 int reduce_rows_per_iteration(int D, aaren_dtype in);
+hipError_t launch_scan_backward(const BackwardParams &p, int D, hipStream_t stream);
 
 }  // namespace aaren

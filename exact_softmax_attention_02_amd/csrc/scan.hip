@@ -33,7 +33,7 @@
 //    and the look-back stops at an aggregate that holds a start (segmented
 //    scan with head flags).
 // Exponentials are base 2: q is pre-multiplied by scale*log2(e).
-#include "device.h"
+#include "lookback.h"
 
 namespace aaren {
 
@@ -51,34 +51,6 @@ struct ScanShape {
     static_assert(D % 64 == 0, "d = 64 or 128");
 };
 
-// Aggregates a look-back walk may park before it waits for a prefix.
-constexpr int kWindow = 16;
-
-__device__ __forceinline__ bool tag_ok(uint64_t word, uint32_t epoch)
-{
-    return (uint32_t)(word >> 33) == epoch;
-}
-
-__device__ __forceinline__ float word_value(uint64_t word)
-{
-    return __uint_as_float((uint32_t)word);
-}
-
-// Publish a state in column-per-lane layout (lane j holds w[j + 64c]).
-template <int D>
-__device__ __forceinline__ void publish(uint64_t *slot, uint32_t tag, float m, float u,
-                                        const float *w, int lane)
-{
-    const uint64_t hi = (uint64_t)tag << 32;
-#pragma unroll
-    for (int c = 0; c < D / 64; ++c)
-        st_agent(slot + 2 + lane + 64 * c, hi | __float_as_uint(w[c]));
-    if (lane == 0)
-        st_agent(slot + 0, hi | __float_as_uint(m));
-    if (lane == 1)
-        st_agent(slot + 1, hi | __float_as_uint(u));
-}
-
 template <int D, typename Tin, typename Tout, int R, int WAVES, bool SEG>
 __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
 {
@@ -93,9 +65,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     __shared__ __attribute__((aligned(16))) float sh_gw[NG][D];
     __shared__ float sh_cm, sh_cu;
     __shared__ __attribute__((aligned(16))) float sh_cw[D];
-    // aggregates met on the look-back walk, newest first (wave 0 only)
-    __shared__ float sh_win_m[kWindow], sh_win_u[kWindow];
-    __shared__ float sh_win_w[kWindow][D];
+    __shared__ LookbackWindow<D> sh_win;  // wave 0's look-back walk
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -283,75 +253,10 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
                 publish<D>(my, epoch << 1, am, au, aw, lane);
             else
                 publish<D>(my, (epoch << 1) | 1u, am, au, aw, lane);
-            // Walk back to the nearest predecessor with an inclusive prefix (or,
-            // packed batches, an aggregate that holds a sequence start), parking
-            // the aggregates met on the way; then fold them onto it oldest first.
-            // The carry is thus always the left fold A_0 (+) ... (+) A_{j-1},
-            // whatever the timing, and the results are reproducible bit for bit.
-            int64_t pred = tile - p.streams;
-            uint32_t polls = 0;
-            int parked = 0;
-            while (true) {
-                const uint64_t *agg = p.slots + (size_t)pred * 2 * SLOT;
-                const uint64_t *pre = agg + SLOT;
-                uint64_t wp[CPL], wa[CPL];
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    wp[c] = ld_agent(pre + 2 + lane + 64 * c);
-                    wa[c] = ld_agent(agg + 2 + lane + 64 * c);
-                }
-                const uint64_t pmw = ld_agent(pre + 0), puw = ld_agent(pre + 1);
-                const uint64_t amw = ld_agent(agg + 0), auw = ld_agent(agg + 1);
-                bool pre_ok = tag_ok(pmw, epoch) && tag_ok(puw, epoch);
-                bool agg_ok = tag_ok(amw, epoch) && tag_ok(auw, epoch);
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    pre_ok = pre_ok && tag_ok(wp[c], epoch);
-                    agg_ok = agg_ok && tag_ok(wa[c], epoch);
-                }
-                pre_ok = __all(pre_ok);
-                agg_ok = __all(agg_ok);
-                const bool agg_starts = SEG && agg_ok && ((amw >> 32) & 1u);
-                if (pre_ok || agg_starts) {
-                    cm = word_value(pre_ok ? pmw : amw);
-                    cu = word_value(pre_ok ? puw : auw);
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c)
-                        cw[c] = word_value(pre_ok ? wp[c] : wa[c]);
-                    break;
-                }
-                if (agg_ok && parked < kWindow) {
-                    if (pred < p.streams) {  // a first tile never publishes an aggregate
-                        if (lane == 0)
-                            __hip_atomic_fetch_or(p.header + kError, 2u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                    // every lane writes the same m, u and reads back only what it wrote
-                    sh_win_m[parked] = word_value(amw);
-                    sh_win_u[parked] = word_value(auw);
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c)
-                        sh_win_w[parked][lane + 64 * c] = word_value(wa[c]);
-                    ++parked;
-                    pred -= p.streams;
-                    continue;
-                }
-                if (++polls > kMaxPolls) {  // bounded wait: give up rather than hang
-                    if (lane == 0)
-                        __hip_atomic_fetch_or(p.header + kError, 4u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            for (int i = parked - 1; i >= 0; --i) {
-                float yw[CPL];
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
-                    yw[c] = sh_win_w[i][lane + 64 * c];
-                combine<CPL>(cm, cu, cw, sh_win_m[i], sh_win_u[i], yw, cm, cu, cw);
-            }
+            // the carry is the left fold A_0 (+) ... (+) A_{j-1} of the stream's
+            // earlier aggregates (from its last sequence start, packed batches)
+            lookback<D, SEG, false>(p.slots, tile - p.streams, -p.streams, p.num_tiles, epoch,
+                                    lane, p.header, sh_win, cm, cu, cw);
         }
         // inclusive prefix = carry (+) aggregate, unless the tile holds a start
         float im = am, iu = au, iw[CPL];

@@ -1,0 +1,316 @@
+// Gradients of the many-to-many scan: dq, dk, dv from dloss/do.
+//
+// The pages present the many-to-many form as differentiable and trained in
+// parallel ("Attention as an RNN" review, proposed method; the
+// memory-efficient-attention review reports differentiation in its abstract
+// and section 5.2, whose body is lost) but print no formula. Derived from the
+// definition o_k = sum_{i<=k} p_ki v_i, p_ki = e^{s_i - L_k},
+// L_k = ln sum_{j<=k} e^{s_j}, with g_k = dloss/do_k and delta_k = <g_k, o_k>:
+//   dv_i = e^{s_i} sum_{k>=i} e^{-L_k} g_k
+//   ds_i = <dv_i, v_i> - e^{s_i} sum_{k>=i} e^{-L_k} delta_k
+//   dk_i = scale ds_i q,   dq = scale sum_i ds_i k_i.
+// Both sums are suffix sums of leaves (m = -L_k, u = delta_k, w = g_k) under
+// the same (m, u, w) combine as the forward scan (weights relative to the
+// largest exponent), so the backward is the forward's machinery run from the
+// end of each stream: tiles are claimed last-first, the look-back walks
+// towards later tiles, pass 2 walks each group's rows backwards. L_k comes
+// from the forward pass (aaren_scan's lse output).
+//
+// One HBM pass: K, V, O, dO read and dK, dV written once (plus 4 bytes of L
+// per row); each tile leaves one partial dq, summed per head in a fixed order
+// by a second kernel, so dq is reproducible bit for bit.
+#include "lookback.h"
+
+namespace aaren {
+
+template <int D>
+struct BackwardShape {
+    static constexpr int E = 4;              // fp32: 4 columns per lane
+    static constexpr int L = D / E;          // lanes per row
+    static constexpr int GPW = 64 / L;
+    static constexpr int WAVES = D == 64 ? 4 : 8;
+    static constexpr int NG = WAVES * GPW;   // 16 groups
+    static constexpr int R = 8;
+    static constexpr int ROWS = NG * R;
+    static constexpr int CPL = D / 64;
+    static_assert(ROWS == backward_tile_rows(D), "tile rows disagree with the workspace sizing");
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * BackwardShape<D>::WAVES) void scan_backward_kernel(
+    const BackwardParams p)
+{
+    using S = BackwardShape<D>;
+    using SL = Slice<D, float>;
+    constexpr int E = S::E, L = S::L, GPW = S::GPW, NG = S::NG, R = S::R, ROWS = S::ROWS;
+    constexpr int SLOT = slot_words(D), CPL = S::CPL;
+
+    __shared__ uint32_t sh_chunk;
+    __shared__ float sh_gm[NG], sh_gu[NG];
+    __shared__ __attribute__((aligned(16))) float sh_gw[NG][D];
+    __shared__ float sh_cm, sh_cu;
+    __shared__ __attribute__((aligned(16))) float sh_cw[D];
+    __shared__ LookbackWindow<D> sh_win;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int gl = lane % L, grp = wave * GPW + lane / L;
+
+    // position along the stream counted from its end (see the forward scan)
+    const uint32_t stream32 = (blockIdx.x / p.group) % (uint32_t)p.streams;
+    if (tid == 0)
+        sh_chunk = __builtin_amdgcn_atomic_inc32(p.counters + (size_t)stream32 * kCounterStride,
+                                                 p.chunks_padded - 1u, __ATOMIC_RELAXED, "agent");
+    __syncthreads();
+    const uint32_t ticket = __builtin_amdgcn_readfirstlane(sh_chunk);
+    const uint32_t epoch = p.epoch;
+    if (ticket >= (uint32_t)p.chunks && ticket < p.chunks_padded)
+        return;  // a padding position: nothing to do
+    if (ticket >= (uint32_t)p.chunks) {
+        if (tid == 0)
+            __hip_atomic_fetch_or(p.header + kError, 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const int64_t chunk = p.chunks - 1 - ticket, stream = stream32;
+    const int64_t tile = chunk * p.streams + stream;
+    const int64_t row0 = chunk * ROWS + (int64_t)grp * R;
+    const int64_t left = p.N - row0;
+    const int nvalid = left <= 0 ? 0 : (left >= R ? R : (int)left);
+
+    const int64_t base = (stream * p.N + row0) * D;  // column 0 of the group's first row
+    u32x4 kr[R], gr[R], orr[R], vr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        kr[r] = gr[r] = orr[r] = vr[r] = u32x4{0, 0, 0, 0};
+        if (r < nvalid) {
+            kr[r] = load_slice<D, float, true>(p.k + base + r * D, gl);
+            gr[r] = load_slice<D, float, true>(p.g + base + r * D, gl);
+            orr[r] = load_slice<D, float, true>(p.o + base + r * D, gl);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < nvalid)
+            vr[r] = load_slice<D, float, true>(p.v + base + r * D, gl);
+    float lm[R];  // leaf exponent -L_r, log2 units
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        lm[r] = (r < nvalid) ? -p.lse[stream * p.N + row0 + r] * kLog2e : kNegInf;
+
+    float qv[E], qs[E];
+    widen<float>(load_slice<D, float, false>(p.q + (stream % p.H) * D, gl), qv);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        qs[e] = qv[e] * p.qscale;
+
+    // scores (log2 units) and delta_r = <g_r, o_r>
+    float s[R], dl[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float kf[E], gf[E], of[E];
+        widen<float>(kr[r], kf);
+        widen<float>(gr[r], gf);
+        widen<float>(orr[r], of);
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            a = __builtin_fmaf(qs[e], kf[e], a);
+            b = __builtin_fmaf(gf[e], of[e], b);
+        }
+        s[r] = group_sum<L>(a);
+        dl[r] = group_sum<L>(b);
+    }
+
+    // ---- pass 1: the group's suffix aggregate, maximum first ------------------
+    float gm = kNegInf;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        gm = fmaxf(gm, lm[r]);
+    float gu = 0.f, gwv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        gwv[e] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float f = (r < nvalid) ? exp2_fast(lm[r] - gm) : 0.f;
+        float gf[E];
+        widen<float>(gr[r], gf);
+        gu = __builtin_fmaf(f, dl[r], gu);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            gwv[e] = __builtin_fmaf(f, gf[e], gwv[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        sh_gw[grp][SL::col(gl, e)] = gwv[e];
+    if (gl == 0) {
+        sh_gm[grp] = gm;
+        sh_gu[grp] = gu;
+    }
+    __syncthreads();
+
+    // state of the groups after this one in the tile: G_{g+1} (+) ... (+) G_{NG-1}
+    auto later_groups = [&](float &xm, float &xu, float *xw) {
+        xm = kNegInf;
+        xu = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            xw[e] = 0.f;
+        for (int g = NG - 1; g > grp; --g) {
+            float yw[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                yw[e] = sh_gw[g][SL::col(gl, e)];
+            combine<E>(sh_gm[g], sh_gu[g], yw, xm, xu, xw, xm, xu, xw);
+        }
+    };
+
+    float pm, pu, pw[E];
+    if (wave != 0)
+        later_groups(pm, pu, pw);
+
+    if (wave == 0) {
+        // tile aggregate, column-per-lane, folded from the last group
+        float am = kNegInf, au = 0.f, aw[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            aw[c] = 0.f;
+        for (int g = NG - 1; g >= 0; --g) {
+            float yw[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                yw[c] = sh_gw[g][lane + 64 * c];
+            combine<CPL>(sh_gm[g], sh_gu[g], yw, am, au, aw, am, au, aw);
+        }
+        uint64_t *my = p.slots + (size_t)tile * 2 * SLOT;
+        float cm = kNegInf, cu = 0.f, cw[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            cw[c] = 0.f;
+        if (chunk < p.chunks - 1) {
+            publish<D>(my, epoch << 1, am, au, aw, lane);
+            // the carry is A_{j+1} (+) ... (+) A_last, the stream's later aggregates
+            lookback<D, false, true>(p.slots, tile + p.streams, p.streams, p.num_tiles, epoch,
+                                     lane, p.header, sh_win, cm, cu, cw);
+        }
+        float im, iu, iw[CPL];
+        combine<CPL>(am, au, aw, cm, cu, cw, im, iu, iw);
+        publish<D>(my + SLOT, epoch << 1, im, iu, iw, lane);
+        if (lane == 0) {
+            sh_cm = cm;
+            sh_cu = cu;
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            sh_cw[lane + 64 * c] = cw[c];
+        later_groups(pm, pu, pw);
+    }
+    __syncthreads();
+
+    // ---- pass 2: rows last-first from (later groups (+) carry) ----------------
+    float xm, xu, xw[E];
+    {
+        float cw[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            cw[e] = sh_cw[SL::col(gl, e)];
+        combine<E>(pm, pu, pw, sh_cm, sh_cu, cw, xm, xu, xw);
+    }
+    float dq_acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        dq_acc[e] = 0.f;
+#pragma unroll
+    for (int r = R - 1; r >= 0; --r) {
+        if (r < nvalid) {
+            float gf[E], vf[E], kf[E];
+            widen<float>(gr[r], gf);
+            widen<float>(vr[r], vf);
+            widen<float>(kr[r], kf);
+            combine<E>(lm[r], dl[r], gf, xm, xu, xw, xm, xu, xw);  // leaf (+) state
+            const float pw_r = exp2_fast(s[r] + xm);  // e^{s_r} times the state's scale
+            float dv[E], part = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                dv[e] = pw_r * xw[e];
+                part = __builtin_fmaf(dv[e], vf[e], part);
+            }
+            const float ds = group_sum<L>(part) - pw_r * xu;
+            const float sds = p.scale * ds;
+            float dk[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                dk[e] = sds * qv[e];
+                dq_acc[e] = __builtin_fmaf(sds, kf[e], dq_acc[e]);
+            }
+            store_slice<D, float, float>(p.dv + base + r * D, gl, dv);
+            store_slice<D, float, float>(p.dk + base + r * D, gl, dk);
+        }
+    }
+
+    // ---- the tile's partial dq: groups summed in a fixed order ----------------
+    __syncthreads();  // sh_gw is free again
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        sh_gw[grp][SL::col(gl, e)] = dq_acc[e];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            float acc = 0.f;
+            for (int g = 0; g < NG; ++g)
+                acc += sh_gw[g][lane + 64 * c];
+            p.dq_partial[(size_t)tile * D + lane + 64 * c] = acc;
+        }
+    }
+}
+
+// dq[h] = sum of the partials of every tile of head h, in a fixed order.
+constexpr int kDqThreads = 1024;
+
+template <int D>
+__global__ __launch_bounds__(kDqThreads) void scan_backward_dq_kernel(const BackwardParams p)
+{
+    constexpr int SUB = kDqThreads / D;
+    __shared__ float sh[SUB][D];
+    const int tid = threadIdx.x, col = tid % D, sub = tid / D;
+    const int64_t h = blockIdx.x;
+    const int64_t B = p.streams / p.H;
+    const int64_t count = B * p.chunks;  // tiles of this head
+    float acc = 0.f;
+#pragma unroll 8
+    for (int64_t i = sub; i < count; i += SUB) {
+        const int64_t b = i / p.chunks, chunk = i - b * p.chunks;
+        const int64_t tile = chunk * p.streams + b * p.H + h;
+        acc += p.dq_partial[(size_t)tile * D + col];
+    }
+    sh[sub][col] = acc;
+    __syncthreads();
+    if (tid < D) {
+        float r = 0.f;
+#pragma unroll
+        for (int s = 0; s < SUB; ++s)
+            r += sh[s][tid];
+        p.dq[h * D + tid] = r;
+    }
+}
+
+template <int D>
+static hipError_t backward_one(const BackwardParams &p, hipStream_t stream)
+{
+    hipLaunchKernelGGL((scan_backward_kernel<D>), dim3((unsigned)(p.streams * p.chunks_padded)),
+                       dim3(64 * BackwardShape<D>::WAVES), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((scan_backward_dq_kernel<D>), dim3((unsigned)p.H), dim3(kDqThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_backward(const BackwardParams &p, int D, hipStream_t stream)
+{
+    return D == 64 ? backward_one<64>(p, stream) : backward_one<128>(p, stream);
+}
+
+}  // namespace aaren

@@ -109,6 +109,28 @@ aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, fl
                         aaren_dtype in_dtype, aaren_dtype out_dtype,
                         void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* ---- gradients of the dense many-to-many scan -------------------------------
+ * "Attention as an RNN" (review, proposed method) presents the many-to-many
+ * form as differentiable and trained in parallel; the pages print no formula.
+ * Derived from the definition, with p_ki = e^{s_i - L_k} and g_k = dloss/do_k:
+ *   dv_i = sum_{k>=i} p_ki g_k
+ *   ds_i = <dv_i, v_i> - sum_{k>=i} p_ki <g_k, o_k>
+ *   dk_i = scale ds_i q_h,  dq_h = scale sum_{b,i} ds_i k_i  (summed over the batch)
+ *   q [H,d], k, v, o, dout [B,H,N,d]  float32 (o and lse from aaren_scan)
+ *   lse [B,H,N] float32: the forward's log-normaliser
+ *   dq [H,d], dk, dv [B,H,N,d] float32 outputs
+ * One pass over K, V, O and dout; dq is reproducible bit for bit. in_dtype
+ * must be AAREN_F32 (others: UNSUPPORTED). The workspace follows the scan
+ * workspace contract (zero-filled once; may be shared with the scans). With
+ * B*H*N == 0, dq is set to zero. */
+size_t aaren_scan_backward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d);
+aaren_status aaren_scan_backward(const void *q, const void *k, const void *v, const void *o,
+                                 const void *dout, const float *lse,
+                                 float *dq, float *dk, float *dv,
+                                 int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                 aaren_dtype in_dtype,
+                                 void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* ---- many-to-many scan, packed variable-length batch -----------------------
  * The same output for a packed batch of independent sequences (each one is
  * scanned on its own; the pages do not treat packed batches, this is the

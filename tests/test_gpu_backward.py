@@ -1,0 +1,118 @@
+"""Gradients of the dense scan on the GPU (forward with lse, then backward)
+against the CPU oracle's float64 gradients."""
+import numpy as np
+import pytest
+import torch
+
+import exact_softmax_attention_02_amd as aaren
+import oracle
+import workloads
+from _gpu import announce, dev, host32
+
+pytestmark = pytest.mark.gpu
+
+
+def run(B, H, N, d, seed, spread=1.0):
+    q, k, v = workloads.dense_inputs(B, H, N, d, seed=seed, device=dev())
+    if spread != 1.0:
+        k = k * spread
+    g = torch.randn(B, H, N, d, device=dev(), generator=torch.Generator(device=dev()).manual_seed(seed + 1))
+    scale = workloads.default_scale(d)
+    o, lse = aaren.aaren_scan(q, k, v, scale, return_lse=True)
+    dq, dk, dv = aaren.aaren_scan_backward(q, k, v, o, g, lse, scale)
+    torch.cuda.synchronize()
+    ref = oracle.scan_backward(host32(q), host32(k), host32(v), host32(g), scale)
+    return (q, k, v, g, scale), (dq, dk, dv), ref
+
+
+def errs(got, ref):
+    out = []
+    for a, b in zip(got, ref):
+        out.append(oracle.max_scaled_err(host32(a), b))
+    return out
+
+
+def dq_bound(q, k, ref_dk, depth):
+    """Bound for dq = sum_i scale ds_i k_i, per column: each term carries the
+    per-row relative error of dk (1e-5) and the sum adds at most `depth`
+    roundings in sequence (8 rows per lane, 16 lane groups, then the partials
+    of a head split 16 ways and the 16 subtotals): (depth 2^-24 + 1e-5) sum_i
+    |scale ds_i| |k_i| (|scale ds_i| = |dk_i| / |q| along q's largest
+    coordinate)."""
+    qh = host32(q).astype(np.float64)
+    kh = host32(k).astype(np.float64)
+    H = qh.shape[0]
+    bound = np.zeros_like(qh)
+    for h in range(H):
+        j = int(np.argmax(np.abs(qh[h])))
+        sds = np.abs(ref_dk[:, h, :, j]) / abs(qh[h, j])            # [B,N]
+        bound[h] = (sds[..., None] * np.abs(kh[:, h])).sum(axis=(0, 1))
+    return (depth * 2.0 ** -24 + 1e-5) * bound
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 64), (1, 1, 2, 64), (2, 3, 127, 64), (1, 2, 128, 64),
+                                     (2, 1, 129, 64), (1, 2, 1000, 64), (2, 2, 3000, 64),
+                                     (1, 1, 300, 128), (2, 2, 1000, 128)])
+def test_backward_matches_oracle(B, H, N, d):
+    announce(f"backward B={B} H={H} N={N} d={d}")
+    (q, k, v, g, scale), got, ref = run(B, H, N, d, seed=70 + N)
+    e_dq, e_dk, e_dv = errs(got, ref)
+    print(f"backward {B}x{H}x{N}x{d}: dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
+    assert e_dk <= 1e-5 and e_dv <= 1e-5, (e_dk, e_dv)
+    chunks = -(-N // 128)
+    depth = 8 + 16 + -(-B * chunks // 16) + 16
+    diff = np.abs(host32(got[0]).astype(np.float64) - ref[0])
+    assert np.all(diff <= dq_bound(q, k, ref[1], depth) + 1e-7), diff.max()
+
+
+def test_backward_large_spread():
+    """Keys stretched 6x: scores reach |s| ~ 25, and the fp32 dot product's
+    rounding (about |s| sqrt(d) 2^-24 per score) moves every weight by that
+    factor: bound 8 |s|max sqrt(d) 2^-24."""
+    announce("backward spread")
+    (q, k, v, g, scale), got, ref = run(1, 2, 2000, 64, seed=90, spread=6.0)
+    e_dq, e_dk, e_dv = errs(got, ref)
+    smax = float((k @ q[None, :, :, None]).abs().max()) * scale
+    tol = max(1e-5, 8 * smax * 8 * 2.0 ** -24)
+    print(f"backward spread: |s| <= {smax:.1f}, tol {tol:.1e}: dq {e_dq:.2e} dk {e_dk:.2e} dv {e_dv:.2e}")
+    assert e_dk <= tol and e_dv <= tol, (e_dk, e_dv)
+
+
+def test_backward_reproducible_and_empty():
+    announce("backward determinism")
+    B, H, N, d = 2, 2, 5000, 64
+    q, k, v = workloads.dense_inputs(B, H, N, d, seed=91, device=dev())
+    g = torch.randn_like(k)
+    o, lse = aaren.aaren_scan(q, k, v, return_lse=True)
+    first = aaren.aaren_scan_backward(q, k, v, o, g, lse)
+    for _ in range(5):
+        again = aaren.aaren_scan_backward(q, k, v, o, g, lse)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(first, again))
+    # no rows: dq is zero
+    z = torch.zeros(2, 0, 64, device=dev()).reshape(1, 2, 0, 64)
+    dq = torch.full((2, 64), 7.0, device=dev())
+    aaren.aaren_scan_backward(q[:2], z, z, z, z, torch.zeros(1, 2, 0, device=dev()), dq=dq)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, torch.zeros_like(dq))
+
+
+def test_forward_lse_matches_oracle():
+    announce("forward lse")
+    for (B, H, N, d, dt) in [(2, 3, 1000, 64, "f32"), (1, 2, 700, 128, "bf16"), (1, 1, 1, 64, "f32")]:
+        q, k, v = workloads.dense_inputs(B, H, N, d, seed=N, device=dev(), dtype=dt)
+        o, lse = aaren.aaren_scan(q, k, v, return_lse=True)
+        _, m, L = oracle.scan(host32(q), host32(k), host32(v), workloads.default_scale(d), stats=True)
+        torch.cuda.synchronize()
+        assert oracle.max_scaled_err(host32(lse), L) <= 1e-5
+
+
+def test_segmented_lse_matches_oracle():
+    announce("segmented lse")
+    lengths = np.array([3, 1, 400, 0, 77])
+    q, k, v, offs = workloads.segmented_inputs(lengths, 3, 64, seed=5, device=dev())
+    o, lse = aaren.aaren_scan_segmented(q, k, v, offs, return_lse=True)
+    _, m, L = oracle.scan_segmented(host32(q), host32(k), host32(v), offs.cpu().numpy(),
+                                    workloads.default_scale(64), stats=True)
+    torch.cuda.synchronize()
+    assert oracle.max_scaled_err(host32(lse), L) <= 1e-5
