@@ -49,7 +49,8 @@ MAX_SETS = 8
 def n_sets(bytes_per_step: int) -> int:
     return max(1, min(MAX_SETS, -(-ROTATE_BYTES // bytes_per_step)))
 KERNEL_SOURCES = {
-    "scan": ["scan.hip", "device.h", "layout.h"],
+    "scan": ["scan.hip", "lookback.h", "device.h", "layout.h"],
+    "backward": ["scan_backward.hip", "lookback.h", "device.h", "layout.h"],
     "step": ["step.hip", "device.h", "layout.h"],
     "reduce": ["reduce.hip", "device.h", "layout.h"],
 }
@@ -95,7 +96,7 @@ def make(name: str, device):
     b = Workload()
     b.name = name
     if name != "copy":
-        w = wl.WORKLOADS[name]
+        w = wl.WORKLOADS["dense" if name == "backward" else name]
         z = w.sizes
         b.describe = w.describe()
         b.dtype = {"f32": "f32", "bf16": "bf16->f32"}[w.dtype]
@@ -123,6 +124,51 @@ def make(name: str, device):
         b.dtype = "f32"
         b.describe = "copy"
         b.cpu = None
+        return b
+
+    if name == "backward":
+        # gradients of the dense batch: the forward's o and lse are inputs
+        B, H, N, d = z["B"], z["H"], z["N"], z["d"]
+        q, k, v = wl.dense_inputs(B, H, N, d, w.seed, device=device)
+        scale = wl.default_scale(d)
+        o, lse = aaren.aaren_scan(q, k, v, scale, return_lse=True)
+        g = torch.randn(B, H, N, d, device=device,
+                        generator=torch.Generator(device=device).manual_seed(w.seed + 100))
+        dq = torch.empty(H, d, device=device)
+        ws = torch.zeros(aaren.aaren_scan_backward_workspace_size(B, H, N, d), dtype=torch.uint8,
+                         device=device)
+        b.bytes_per_launch = 6 * k.numel() * 4 + lse.numel() * 4 + dq.numel() * 4
+        b.sets = n_sets(b.bytes_per_launch)
+        bufs = [(k, v, o, g, lse, torch.empty_like(k), torch.empty_like(v))]
+        bufs += [tuple(x.clone() for x in bufs[0][:5]) + (torch.empty_like(k), torch.empty_like(v))
+                 for _ in range(b.sets - 1)]
+        turn = [0]
+
+        def step():
+            kk, vv, oo, gg, ll, dk, dv = bufs[turn[0] % b.sets]
+            turn[0] += 1
+            aaren.aaren_scan_backward(q, kk, vv, oo, gg, ll, scale, dq=dq, dk=dk, dv=dv,
+                                      workspace=ws)
+        b.step = step
+        b.kind = "backward"
+        b.units = B * H * N
+        b.launches_per_step = 1
+        b.config = {"workload": f"gradients of the dense many-to-many scan {b.describe}", "B": B,
+                    "H": H, "N": N, "d": d, "in_dtype": "f32", "out_dtype": "f32"}
+        b.kernel = "scan_backward_kernel + scan_backward_dq_kernel"
+
+        def cpu(budget_s):
+            import oracle
+            qh, kh, vh, gh = (t.cpu().numpy() for t in (q, k, v, g))
+            done, t0 = 0, time.perf_counter()
+            while True:
+                oracle.scan_backward(qh, kh, vh, gh, scale)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return done * B * H * N / dt, f"{done} pass(es) over {B}x{H}x{N} (d={d}) gradients"
+        b.cpu = cpu
         return b
 
     if w.kind == "dense":
@@ -285,7 +331,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
                     choices=["single", "dense", "long_bf16", "ragged", "stream", "reduce",
-                             "copy"])
+                             "backward", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle time budget for cpu_baseline (0 to skip)")
     args = ap.parse_args()

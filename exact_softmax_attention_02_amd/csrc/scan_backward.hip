@@ -36,9 +36,11 @@ struct BackwardShape {
     static_assert(ROWS == backward_tile_rows(D), "tile rows disagree with the workspace sizing");
 };
 
+// Five row tensors per lane: without a bound the compiler keeps values in
+// AGPRs and runs one wave per SIMD; three waves fit without spilling.
 template <int D>
-__global__ __launch_bounds__(64 * BackwardShape<D>::WAVES) void scan_backward_kernel(
-    const BackwardParams p)
+__global__ __launch_bounds__(64 * BackwardShape<D>::WAVES)
+__attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const BackwardParams p)
 {
     using S = BackwardShape<D>;
     using SL = Slice<D, float>;

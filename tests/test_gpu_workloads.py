@@ -127,3 +127,29 @@ def test_reduce_in_full():
     L = host32(m).astype(np.float64) + np.log(host32(u).astype(np.float64))
     assert np.max(np.abs(L - rl) / (1 + np.abs(rl))) <= 1e-5
     print(f"reduce: max scaled err {err:.3e}")
+
+
+def test_dense_gradients_in_full():
+    """Gradients at the dense batch's full size (the backward bench's shape)."""
+    w = W["dense"]
+    sz = w.sizes
+    B, H, N, d = sz["B"], sz["H"], sz["N"], sz["d"]
+    announce(f"workload dense gradients: {w.describe()}")
+    q, k, v = workloads.dense_inputs(B, H, N, d, w.seed, device=dev())
+    g = torch.randn(B, H, N, d, device=dev(), generator=torch.Generator(device=dev()).manual_seed(w.seed + 100))
+    scale = workloads.default_scale(d)
+    o, lse = aaren.aaren_scan(q, k, v, scale, return_lse=True)
+    dq, dk, dv = aaren.aaren_scan_backward(q, k, v, o, g, lse, scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.scan_backward(host32(q), host32(k), host32(v), host32(g), scale)
+    e_k = check(dk, rk, 1e-5, "dk")
+    e_v = check(dv, rv, 1e-5, "dv")
+    # dq sums B*N = 131072 terms per head: bound as in test_gpu_backward.dq_bound
+    qh, kh = host32(q).astype(np.float64), host32(k).astype(np.float64)
+    depth = 8 + 16 + -(-B * (N // 128) // 16) + 16
+    for h in range(H):
+        j = int(np.argmax(np.abs(qh[h])))
+        sds = np.abs(rk[:, h, :, j]) / abs(qh[h, j])
+        bound = (depth * 2.0 ** -24 + 1e-5) * (sds[..., None] * np.abs(kh[:, h])).sum(axis=(0, 1))
+        assert np.all(np.abs(host32(dq[h]) - rq[h]) <= bound + 1e-7)
+    print(f"dense gradients: dk {e_k:.3e} dv {e_v:.3e}")
