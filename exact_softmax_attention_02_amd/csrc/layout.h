@@ -130,7 +130,7 @@ struct BackwardParams {
     const float *lse;        // log-normaliser per row, natural units
     float *dk;
     float *dv;
-    float *dq_partial;       // [tiles][D], one per tile
+    float *dq_partial;       // [H][B][chunks][D], one per tile
     float *dq;               // [H][D]
     int64_t streams;         // B*H
     int64_t H;

@@ -80,46 +80,33 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
     const int nvalid = left <= 0 ? 0 : (left >= R ? R : (int)left);
 
     const int64_t base = (stream * p.N + row0) * D;  // column 0 of the group's first row
-    u32x4 kr[R], gr[R], orr[R], vr[R];
+    // dO and O first: the tile's aggregate needs only them and L, so it is
+    // published (and the look-back chain moves on) before K and V arrive
+    u32x4 gr[R], orr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        kr[r] = gr[r] = orr[r] = vr[r] = u32x4{0, 0, 0, 0};
+        gr[r] = orr[r] = u32x4{0, 0, 0, 0};
         if (r < nvalid) {
-            kr[r] = load_slice<D, float, true>(p.k + base + r * D, gl);
             gr[r] = load_slice<D, float, true>(p.g + base + r * D, gl);
             orr[r] = load_slice<D, float, true>(p.o + base + r * D, gl);
         }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (r < nvalid)
-            vr[r] = load_slice<D, float, true>(p.v + base + r * D, gl);
     float lm[R];  // leaf exponent -L_r, log2 units
 #pragma unroll
     for (int r = 0; r < R; ++r)
         lm[r] = (r < nvalid) ? -p.lse[stream * p.N + row0 + r] * kLog2e : kNegInf;
 
-    float qv[E], qs[E];
-    widen<float>(load_slice<D, float, false>(p.q + (stream % p.H) * D, gl), qv);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-        qs[e] = qv[e] * p.qscale;
-
-    // scores (log2 units) and delta_r = <g_r, o_r>
-    float s[R], dl[R];
+    // delta_r = <g_r, o_r>
+    float dl[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        float kf[E], gf[E], of[E];
-        widen<float>(kr[r], kf);
+        float gf[E], of[E];
         widen<float>(gr[r], gf);
         widen<float>(orr[r], of);
-        float a = 0.f, b = 0.f;
+        float b = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            a = __builtin_fmaf(qs[e], kf[e], a);
+        for (int e = 0; e < E; ++e)
             b = __builtin_fmaf(gf[e], of[e], b);
-        }
-        s[r] = group_sum<L>(a);
         dl[r] = group_sum<L>(b);
     }
 
@@ -149,6 +136,18 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
         sh_gm[grp] = gm;
         sh_gu[grp] = gu;
     }
+    // K and V land during the barrier and the look-back (O's registers are free)
+    u32x4 kr[R], vr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        kr[r] = vr[r] = u32x4{0, 0, 0, 0};
+        if (r < nvalid)
+            kr[r] = load_slice<D, float, true>(p.k + base + r * D, gl);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < nvalid)
+            vr[r] = load_slice<D, float, true>(p.v + base + r * D, gl);
     __syncthreads();
 
     // state of the groups after this one in the tile: G_{g+1} (+) ... (+) G_{NG-1}
@@ -209,6 +208,24 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
     }
     __syncthreads();
 
+    // scores, log2 units
+    float qv[E], qs[E];
+    widen<float>(load_slice<D, float, false>(p.q + (stream % p.H) * D, gl), qv);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        qs[e] = qv[e] * p.qscale;
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float kf[E];
+        widen<float>(kr[r], kf);
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            a = __builtin_fmaf(qs[e], kf[e], a);
+        s[r] = group_sum<L>(a);
+    }
+
     // ---- pass 2: rows last-first from (later groups (+) carry) ----------------
     float xm, xu, xw[E];
     {
@@ -257,40 +274,49 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
         sh_gw[grp][SL::col(gl, e)] = dq_acc[e];
     __syncthreads();
     if (wave == 0) {
+        // partials of one head are contiguous: [H][B][chunks][D]
+        const int64_t B = p.streams / p.H;
+        const int64_t at = ((stream % p.H) * B + stream / p.H) * p.chunks + chunk;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             float acc = 0.f;
             for (int g = 0; g < NG; ++g)
                 acc += sh_gw[g][lane + 64 * c];
-            p.dq_partial[(size_t)tile * D + lane + 64 * c] = acc;
+            p.dq_partial[(size_t)at * D + lane + 64 * c] = acc;
         }
     }
 }
 
-// dq[h] = sum of the partials of every tile of head h, in a fixed order.
+// dq[h] = sum of the B*chunks partials of head h, in a fixed order: thread
+// (sub, c4) adds rows sub, sub + SUB, ... of columns 4c4..4c4+3, then the SUB
+// subtotals are added in order.
 constexpr int kDqThreads = 1024;
 
 template <int D>
 __global__ __launch_bounds__(kDqThreads) void scan_backward_dq_kernel(const BackwardParams p)
 {
-    constexpr int SUB = kDqThreads / D;
-    __shared__ float sh[SUB][D];
-    const int tid = threadIdx.x, col = tid % D, sub = tid / D;
+    constexpr int V4 = D / 4, SUB = kDqThreads / V4;
+    __shared__ __attribute__((aligned(16))) float sh[SUB][D];
+    const int tid = threadIdx.x, c4 = tid % V4, sub = tid / V4;
     const int64_t h = blockIdx.x;
-    const int64_t B = p.streams / p.H;
-    const int64_t count = B * p.chunks;  // tiles of this head
-    float acc = 0.f;
+    const int64_t count = (p.streams / p.H) * p.chunks;  // partials of this head
+    const float *src = p.dq_partial + (size_t)h * count * D + 4 * c4;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int64_t i = sub; i < count; i += SUB) {
-        const int64_t b = i / p.chunks, chunk = i - b * p.chunks;
-        const int64_t tile = chunk * p.streams + b * p.H + h;
-        acc += p.dq_partial[(size_t)tile * D + col];
+        float x[4];
+        widen<float>(load16(src + (size_t)i * D), x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            a[e] += x[e];
     }
-    sh[sub][col] = acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        sh[sub][4 * c4 + e] = a[e];
     __syncthreads();
     if (tid < D) {
         float r = 0.f;
-#pragma unroll
+#pragma unroll 8
         for (int s = 0; s < SUB; ++s)
             r += sh[s][tid];
         p.dq[h * D + tid] = r;

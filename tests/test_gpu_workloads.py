@@ -146,7 +146,7 @@ def test_dense_gradients_in_full():
     e_v = check(dv, rv, 1e-5, "dv")
     # dq sums B*N = 131072 terms per head: bound as in test_gpu_backward.dq_bound
     qh, kh = host32(q).astype(np.float64), host32(k).astype(np.float64)
-    depth = 8 + 16 + -(-B * (N // 128) // 16) + 16
+    depth = 8 + 16 + -(-B * (N // 128) // 32) + 64
     for h in range(H):
         j = int(np.argmax(np.abs(qh[h])))
         sds = np.abs(rk[:, h, :, j]) / abs(qh[h, j])
