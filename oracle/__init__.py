@@ -139,6 +139,21 @@ def step(q, k_t, v_t, state, scale):
     return o
 
 
+def append(q, k, v, state, scale):
+    """Append T tokens to every (stream, head) state: k, v [T,S,H,d]
+    (time-major, k[t] is one step's keys), state = (m, u, w) float64 updated
+    in place; returns o [T,S,H,d] float64, o[t] the output after token t.
+
+    By definition T successive single-pair updates: the RNN view of the
+    "Attention as an RNN" review (abstract item (ii), proposed method) absorbs
+    new tokens one at a time into the constant-size state."""
+    k, v = _f32(k), _f32(v)
+    out = np.empty(k.shape, np.float64)
+    for t in range(k.shape[0]):
+        out[t] = step(q, k[t], v[t], state, scale)
+    return out
+
+
 def reduce(q, k, v, scale, stats: bool = False):
     """Many-to-one output. q [H,d], k,v [B,H,N,d] -> o [B,H,d] float64
     (and m, L [B,H] with stats)."""

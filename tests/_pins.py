@@ -254,6 +254,31 @@ def check_step(orc, seed=20):
     assert np.array_equal(o, outs[-1]) and all(np.array_equal(a, b) for a, b in zip(resumed, st))
 
 
+def check_append(orc, seed=25):
+    """Appending tokens in blocks of any size continues the same scan: from a
+    state that already holds a prefix, each appended token's output and the
+    final log-normaliser equal brute force over prefix + appended tokens
+    (sizes S, H, T, d all distinct so a swapped axis shows)."""
+    rng = _rng(seed)
+    S, H, d, T0, T1 = 4, 3, 8, 7, 11
+    q = rng.standard_normal((H, d)).astype(np.float32)
+    k = (2 * rng.standard_normal((T0 + T1, S, H, d))).astype(np.float32)
+    v = rng.standard_normal((T0 + T1, S, H, d)).astype(np.float32)
+    scale = 0.3
+    st = orc.state_init(S, H, d)
+    first = orc.append(q, k[:T0], v[:T0], st, scale)
+    second = orc.append(q, k[T0:], v[T0:], st, scale)
+    assert first.shape == (T0, S, H, d) and second.shape == (T1, S, H, d)
+    ref = brute.brute_scan_batch(q, k.transpose(1, 2, 0, 3), v.transpose(1, 2, 0, 3), scale)
+    got = np.concatenate([first, second]).transpose(1, 2, 0, 3)      # [S,H,T,d]
+    _close(got, ref, 1e-12, "blocked appends vs brute scan")
+    s_all = np.stack([[brute.scores(q[h], k[:, s, h], scale) for h in range(H)] for s in range(S)])
+    _close(st[0] + np.log(st[1]), logsumexp(s_all, axis=-1), 1e-13, "append log-normaliser")
+    _close(st[0], s_all.max(axis=-1), 1e-13, "m is the running maximum of the scores")
+    empty = orc.append(q, k[:0], v[:0], st, scale)
+    assert empty.shape == (0, S, H, d)
+
+
 def check_segmented(orc, seed=21):
     """Each packed sequence is scanned on its own: == brute force per segment;
     empty and length-1 segments included."""
@@ -358,5 +383,5 @@ def check_backward_closed_forms(orc, seed=24):
 
 ALL = [check_golden, check_scan_vs_definition, check_stats, check_single_token,
        check_running_mean, check_two_tokens, check_dominating_key, check_shift_invariance,
-       check_convex_hull, check_bracketing, check_reduce, check_step, check_segmented,
+       check_convex_hull, check_bracketing, check_reduce, check_step, check_append, check_segmented,
        check_backward, check_backward_finite_differences, check_backward_closed_forms]

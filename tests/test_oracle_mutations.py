@@ -5,6 +5,7 @@ import ctypes
 import os
 import subprocess
 
+import numpy as np
 import pytest
 
 import oracle
@@ -117,3 +118,39 @@ def test_mutant_is_caught(tmp_path, name, func, old, new):
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(check.__name__)
     assert caught, f"no pin catches the planted mistake '{name}'"
+
+
+def _append_dropping_last(q, k, v, state, scale):
+    out = np.zeros(np.shape(k), np.float64)
+    for t in range(max(np.shape(k)[0] - 1, 0)):
+        out[t] = oracle.step(q, k[t], v[t], state, scale)
+    return out
+
+
+def _append_previous_value(q, k, v, state, scale):
+    out = np.empty(np.shape(k), np.float64)
+    for t in range(np.shape(k)[0]):
+        out[t] = oracle.step(q, k[t], v[max(t - 1, 0)], state, scale)
+    return out
+
+
+def _append_on_a_copy(q, k, v, state, scale):
+    return oracle.append(q, k, v, tuple(a.copy() for a in state), scale)
+
+
+class _AppendMutant:
+    """The oracle with its append replaced by a mistaken one."""
+
+    def __init__(self, fn):
+        self.append = fn
+
+    def __getattr__(self, name):
+        return getattr(oracle, name)
+
+
+@pytest.mark.parametrize("fn", [_append_dropping_last, _append_previous_value, _append_on_a_copy],
+                         ids=["append drops the last token", "append pairs k_t with v_(t-1)",
+                              "append leaves the caller's state unchanged"])
+def test_append_mutant_is_caught(fn):
+    with pytest.raises((AssertionError, ValueError)):
+        _pins.check_append(_AppendMutant(fn))
