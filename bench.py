@@ -9,6 +9,9 @@ already resident in HBM:
   ragged                   : one aaren_scan_segmented call (token-heads = H*T)
   stream                   : aaren_state_init + 256 aaren_step calls
                                                            (token-heads = S*H*256)
+  append                   : aaren_state_init + 16 aaren_append calls of 16
+                             tokens, the same 256 tokens per stream
+  backward                 : one aaren_scan_backward call on the dense batch
   reduce                   : one aaren_reduce call         (keys = B*H*N)
 W untimed steps, then exactly K steps between two HIP events recorded on the
 stream the kernels run on. Prints one JSON line. The default workload is the
@@ -52,6 +55,7 @@ KERNEL_SOURCES = {
     "scan": ["scan.hip", "lookback.h", "device.h", "layout.h"],
     "backward": ["scan_backward.hip", "lookback.h", "device.h", "layout.h"],
     "step": ["step.hip", "device.h", "layout.h"],
+    "append": ["step.hip", "device.h", "layout.h"],
     "reduce": ["reduce.hip", "device.h", "layout.h"],
 }
 
@@ -285,6 +289,46 @@ def make(name: str, device):
             return done * ns * H * T / dt, f"{done} pass(es) over {ns} streams x {H} heads x {T} appends"
         b.cpu = cpu
 
+    elif w.kind == "append":
+        S, H, d, T, blk = z["S"], z["H"], z["d"], z["steps"], z["block"]
+        q, k, v = wl.step_inputs(S, H, d, T, w.seed, device=device)
+        scale = wl.default_scale(d)
+        m, u, st_w = aaren.new_state(S, H, d, device=device)
+        o = torch.empty(blk, S, H, d, device=device)
+
+        def step():
+            aaren.aaren_state_init(m, u, st_w)
+            for t0 in range(0, T, blk):
+                aaren.aaren_append(q, k[t0:t0 + blk], v[t0:t0 + blk], m, u, st_w, scale, o=o)
+        b.step = step
+        b.kind = "append"
+        b.units = S * H * T
+        b.launches_per_step = T // blk
+        # per stream-head and call: blk x (k, v read, o written) rows of d x 4 B,
+        # plus the state (w, m, u) read and written once
+        b.bytes_per_launch = S * H * (blk * 3 * d * 4 + 2 * (d * 4 + 8))
+        b.config = {"workload": f"multi-token append, {T} tokens per stream in {T // blk} calls of "
+                                f"{blk} {b.describe}", "S": S, "H": H, "d": d, "tokens": T,
+                    "tokens_per_call": blk, "in_dtype": "f32", "out_dtype": "f32"}
+        b.kernel = "append_kernel"
+
+        def cpu(budget_s):
+            import oracle
+            ns = 4096
+            qh, kh, vh = q.cpu().numpy(), k[:, :ns].cpu().numpy(), v[:, :ns].cpu().numpy()
+            done, t0 = 0, time.perf_counter()
+            while True:
+                st = oracle.state_init(ns, H, d)
+                for a in range(0, T, blk):
+                    oracle.append(qh, kh[a:a + blk], vh[a:a + blk], st, scale)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return done * ns * H * T / dt, (f"{done} pass(es) over {ns} streams x {H} heads x {T} "
+                                             f"tokens in appends of {blk}")
+        b.cpu = cpu
+
     else:  # reduce
         B, H, N, d = z["B"], z["H"], z["N"], z["d"]
         q, k, v = wl.reduce_inputs(B, H, N, d, w.seed, device=device)
@@ -330,8 +374,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
-                    choices=["single", "dense", "long_bf16", "ragged", "stream", "reduce",
-                             "backward", "copy"])
+                    choices=["single", "dense", "long_bf16", "ragged", "stream", "append",
+                             "reduce", "backward", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle time budget for cpu_baseline (0 to skip)")
     args = ap.parse_args()

@@ -30,7 +30,7 @@ EXPORTS = (
     "aaren_version", "aaren_status_string", "aaren_last_error", "aaren_workspace_clear",
     "aaren_scan_workspace_size", "aaren_scan", "aaren_scan_segmented_workspace_size",
     "aaren_scan_segmented", "aaren_state_init", "aaren_step", "aaren_reduce_workspace_size",
-    "aaren_reduce", "aaren_scan_backward_workspace_size", "aaren_scan_backward",
+    "aaren_reduce", "aaren_scan_backward_workspace_size", "aaren_scan_backward", "aaren_append",
 )
 
 
@@ -59,6 +59,7 @@ def _load():
         "aaren_scan_segmented": (I, [P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
         "aaren_state_init": (I, [P, P, P, I64, I64, I64, P]),
         "aaren_step": (I, [P, P, P, P, P, P, P, I64, I64, I64, F, I, I, P]),
+        "aaren_append": (I, [P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P]),
         "aaren_reduce_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_reduce": (I, [P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
         "aaren_scan_backward_workspace_size": (SZ, [I64, I64, I64, I64]),
@@ -291,6 +292,28 @@ def aaren_step(q, k_t, v_t, m, u, w, scale=None, out_dtype=None, o_t=None, emit=
                           default_scale(d) if scale is None else float(scale),
                           _dtype_code(k_t.dtype), _dtype_code(out_dtype), _stream(dev)))
     return o_t if emit else None
+
+
+def aaren_append(q, k, v, m, u, w, scale=None, out_dtype=None, o=None, emit=True):
+    """Append T pairs per (stream, head) to (m, u, w) in place: k, v [T,S,H,d]
+    time-major; returns o [T,S,H,d] (or None with emit=False)."""
+    dev = _need_cuda(q, k, v, m, u, w, o)
+    T, S, H, d = k.shape
+    if q.shape != (H, d) or v.shape != k.shape or w.shape != (S, H, d):
+        raise ValueError("expected q [H,d], k, v [T,S,H,d], w [S,H,d], m, u [S,H]")
+    if q.dtype != k.dtype or v.dtype != k.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    if m.shape != (S, H) or u.shape != (S, H) or not all(
+            t.dtype == torch.float32 for t in (m, u, w)):
+        raise ValueError("state must be float32 m, u [S,H] and w [S,H,d]")
+    out_dtype = out_dtype or torch.float32
+    if emit and o is None:
+        o = torch.empty(T, S, H, d, dtype=out_dtype, device=dev)
+    _check(lib.aaren_append(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(u), _ptr(w),
+                            _ptr(o if emit else None), S, T, H, d,
+                            default_scale(d) if scale is None else float(scale),
+                            _dtype_code(k.dtype), _dtype_code(out_dtype), _stream(dev)))
+    return o if emit else None
 
 
 def aaren_reduce(q, k, v, scale=None, out_dtype=None, stats=False, out=None, workspace=None):

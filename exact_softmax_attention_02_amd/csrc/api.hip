@@ -528,10 +528,55 @@ AAREN_API aaren_status aaren_step(const void *q, const void *k_t, const void *v_
     p.o = o_t;
     p.units = S * H;
     p.H = H;
+    p.tokens = 1;
     p.scale = scale;
     return hip_status(aaren::launch_step(p, (int)d, in_dtype, out_dtype,
                                          static_cast<hipStream_t>(hip_stream)),
                       "step launch");
+}
+
+AAREN_API aaren_status aaren_append(const void *q, const void *k, const void *v, float *m,
+                                    float *u, float *w, void *o, int64_t S, int64_t T, int64_t H,
+                                    int64_t d, float scale, aaren_dtype in_dtype,
+                                    aaren_dtype out_dtype, void *hip_stream)
+{
+    if (S < 0 || T < 0 || H < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (S %lld, T %lld, H %lld)",
+                    (long long)S, (long long)T, (long long)H);
+    CHECK(check_common(d, in_dtype, out_dtype));
+    const int64_t elems = mul_checked({T, S, H, d});
+    if (elems < 0 || mul_checked({S, H, d}) < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "T*S*H*d overflows");
+    if (elems == 0)
+        return AAREN_OK;
+    CHECK(check_ptr(q, "q"));
+    CHECK(check_ptr(k, "k"));
+    CHECK(check_ptr(v, "v"));
+    CHECK(check_ptr(w, "w"));
+    if (o)
+        CHECK(check_ptr(o, "o"));
+    if (!m || !u)
+        return fail(AAREN_ERR_INVALID_ARG, "m or u is NULL");
+    if ((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(u)) & 3u)
+        return fail(AAREN_ERR_ALIGNMENT, "m or u is not 4-byte aligned");
+    aaren::StepParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.m = m;
+    p.u = u;
+    p.w = w;
+    p.o = o;
+    p.units = S * H;
+    p.H = H;
+    p.tokens = T;
+    p.scale = scale;
+    if (log_enabled())
+        fprintf(stderr, "[aaren] append S=%lld T=%lld H=%lld d=%lld\n", (long long)S,
+                (long long)T, (long long)H, (long long)d);
+    return hip_status(aaren::launch_append(p, (int)d, in_dtype, out_dtype,
+                                           static_cast<hipStream_t>(hip_stream)),
+                      "append launch");
 }
 
 // ---- many-to-one reduction ------------------------------------------------------

@@ -91,8 +91,9 @@ struct StepParams {
     float *u;
     float *w;
     void *o;
-    int64_t units;  // S*H
+    int64_t units;   // S*H
     int64_t H;
+    int64_t tokens;  // appended per unit (1 for a step); k, v, o are [tokens][units][d]
     float scale;
 };
 
@@ -155,6 +156,8 @@ hipError_t launch_segment_flags(const int64_t *offsets, int64_t num_seqs, int64_
 int scan_rows_per_tile(int D, aaren_dtype in);
 hipError_t launch_step(const StepParams &p, int D, aaren_dtype in, aaren_dtype out,
                        hipStream_t stream);
+hipError_t launch_append(const StepParams &p, int D, aaren_dtype in, aaren_dtype out,
+                         hipStream_t stream);
 hipError_t launch_state_init(float *m, float *u, float *w, int64_t units, int64_t D,
                              hipStream_t stream);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);

@@ -11,6 +11,28 @@
 
 namespace aaren {
 
+// Absorb one pair (score s in natural units, value row vf) into the state:
+// the side with the smaller maximum is scaled by e^{lo-hi}, an empty side
+// (maximum -inf) weighs 0. The step and the append kernels share it, so T
+// appended tokens give bit for bit the state and outputs of T steps.
+template <int E>
+__device__ __forceinline__ void absorb_pair(float s, const float *vf, float &m, float &u,
+                                            float *wv)
+{
+    const bool up = s > m;
+    const float hi = up ? s : m;
+    const float lo = up ? m : s;
+    float ex = exp2_fast((lo - hi) * kLog2e);
+    ex = (lo == kNegInf) ? 0.f : ex;
+    const float a = up ? ex : 1.f;
+    const float pr = up ? 1.f : ex;
+    u = __builtin_fmaf(u, a, pr);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        wv[e] = __builtin_fmaf(wv[e], a, pr * vf[e]);
+    m = hi;
+}
+
 template <int D, typename Tin, typename Tout>
 __global__ __launch_bounds__(256) void step_kernel(const StepParams p)
 {
@@ -30,38 +52,121 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p)
     widen<Tin>(load_slice<D, Tin, true>(static_cast<const Tin *>(p.v) + off, gl), vf);
     float *wp = p.w + off;
     load_state<D, Tin>(wp, gl, wv);
-    const float m = p.m[unit], u = p.u[unit];
+    float m = p.m[unit], u = p.u[unit];
 
     float part = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e)
         part = __builtin_fmaf(qv[e] * p.scale, kf[e], part);
-    const float s = group_sum<L>(part);
-
-    // absorb (s, v): the side with the smaller maximum is scaled by e^{lo-hi}
-    const bool up = s > m;
-    const float hi = up ? s : m;
-    const float lo = up ? m : s;
-    float ex = exp2_fast((lo - hi) * kLog2e);
-    ex = (lo == kNegInf) ? 0.f : ex;
-    const float a = up ? ex : 1.f;
-    const float pr = up ? 1.f : ex;
-    const float nu = __builtin_fmaf(u, a, pr);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-        wv[e] = __builtin_fmaf(wv[e], a, pr * vf[e]);
+    absorb_pair<E>(group_sum<L>(part), vf, m, u, wv);
     store_state<D, Tin>(wp, gl, wv);
     if (gl == 0) {
-        p.m[unit] = hi;
-        p.u[unit] = nu;
+        p.m[unit] = m;
+        p.u[unit] = u;
     }
     if (p.o) {
-        const float inv = rcp_fast(nu);
+        const float inv = rcp_fast(u);
         float ov[E];
 #pragma unroll
         for (int e = 0; e < E; ++e)
             ov[e] = wv[e] * inv;
         store_slice<D, Tin, Tout>(static_cast<Tout *>(p.o) + off, gl, ov);
+    }
+}
+
+// Absorb NB consecutive tokens of one (stream, head) into its state held in
+// registers: the block's loads and scores first, then its pairs in order, each
+// emitting o_t = w_t / u_t when EMIT. kp, vp, op point at the block's first
+// row; rows are tstride elements apart.
+template <int D, typename Tin, typename Tout, int NB, bool EMIT>
+__device__ __forceinline__ void append_block(const Tin *kp, const Tin *vp, Tout *op,
+                                             int64_t tstride, int gl, const float *qs, float &m,
+                                             float &u, float *wv)
+{
+    using G = RowGeo<D, Tin>;
+    constexpr int E = G::kElems, L = G::kLanes;
+    u32x4 kr[NB], vr[NB];
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+        kr[r] = load_slice<D, Tin, true>(kp + r * tstride, gl);
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+        vr[r] = load_slice<D, Tin, true>(vp + r * tstride, gl);
+    float s[NB];
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        float kf[E];
+        widen<Tin>(kr[r], kf);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            part = __builtin_fmaf(qs[e], kf[e], part);
+        s[r] = group_sum<L>(part);
+    }
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        float vf[E];
+        widen<Tin>(vr[r], vf);
+        absorb_pair<E>(s[r], vf, m, u, wv);
+        if constexpr (EMIT) {
+            const float inv = rcp_fast(u);
+            float ov[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                ov[e] = wv[e] * inv;
+            store_slice<D, Tin, Tout>(op + r * tstride, gl, ov);
+        }
+    }
+}
+
+// Append `tokens` pairs to every (stream, head): a scan of the new tokens
+// with the stored state as its carry-in, one lane group per (stream, head),
+// walking the tokens in order, loading R at a time, then the remainder one by
+// one. k, v and o are time-major ([t][unit][d], k[t] being one step's keys),
+// so a wavefront reads and writes whole contiguous rows for each token. Each
+// pair is absorbed with the running maximum (the state is never rescaled to a
+// maximum its outputs have not reached yet, which could underflow u), with
+// the step's own arithmetic.
+template <int D, typename Tin, typename Tout, int R, bool EMIT>
+__global__ __launch_bounds__(256) void append_kernel(const StepParams p)
+{
+    using G = RowGeo<D, Tin>;
+    constexpr int E = G::kElems, L = G::kLanes;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t unit = gid / L;
+    const int gl = threadIdx.x % L;
+    if (unit >= p.units)  // whole groups leave together: L divides 256
+        return;
+    const int64_t h = unit % p.H;
+    const int64_t tstride = p.units * D;  // elements from one token's row to the next
+
+    float qs[E], wv[E];
+    widen<Tin>(load_slice<D, Tin, false>(static_cast<const Tin *>(p.q) + h * D, gl), qs);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        qs[e] *= p.scale;
+    float *wp = p.w + unit * D;
+    load_state<D, Tin>(wp, gl, wv);
+    float m = p.m[unit], u = p.u[unit];
+
+    const Tin *kp = static_cast<const Tin *>(p.k) + unit * D;
+    const Tin *vp = static_cast<const Tin *>(p.v) + unit * D;
+    Tout *op = EMIT ? static_cast<Tout *>(p.o) + unit * D : nullptr;
+    int64_t t = 0;
+#pragma unroll 1
+    for (; t + R <= p.tokens; t += R)
+        append_block<D, Tin, Tout, R, EMIT>(kp + t * tstride, vp + t * tstride,
+                                            EMIT ? op + t * tstride : nullptr, tstride, gl, qs,
+                                            m, u, wv);
+#pragma unroll 1
+    for (; t < p.tokens; ++t)
+        append_block<D, Tin, Tout, 1, EMIT>(kp + t * tstride, vp + t * tstride,
+                                            EMIT ? op + t * tstride : nullptr, tstride, gl, qs,
+                                            m, u, wv);
+    store_state<D, Tin>(wp, gl, wv);
+    if (gl == 0) {
+        p.m[unit] = m;
+        p.u[unit] = u;
     }
 }
 
@@ -117,6 +222,39 @@ hipError_t launch_step(const StepParams &p, int D, aaren_dtype in, aaren_dtype o
                        hipStream_t stream)
 {
     return D == 64 ? step_dtypes<64>(p, in, out, stream) : step_dtypes<128>(p, in, out, stream);
+}
+
+template <int D, typename Tin, typename Tout>
+static hipError_t append_one(const StepParams &p, hipStream_t stream)
+{
+    constexpr int L = RowGeo<D, Tin>::kLanes;
+    const int64_t threads = p.units * L;
+    const int64_t blocks = (threads + 255) / 256;
+    if (p.o)
+        hipLaunchKernelGGL((append_kernel<D, Tin, Tout, 8, true>), dim3((unsigned)blocks),
+                           dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((append_kernel<D, Tin, Tout, 8, false>), dim3((unsigned)blocks),
+                           dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t append_dtypes(const StepParams &p, aaren_dtype in, aaren_dtype out,
+                                hipStream_t stream)
+{
+    if (in == AAREN_F32)
+        return out == AAREN_F32 ? append_one<D, float, float>(p, stream)
+                                : append_one<D, float, bf16>(p, stream);
+    return out == AAREN_F32 ? append_one<D, bf16, float>(p, stream)
+                            : append_one<D, bf16, bf16>(p, stream);
+}
+
+hipError_t launch_append(const StepParams &p, int D, aaren_dtype in, aaren_dtype out,
+                         hipStream_t stream)
+{
+    return D == 64 ? append_dtypes<64>(p, in, out, stream)
+                   : append_dtypes<128>(p, in, out, stream);
 }
 
 static unsigned grid_for(int64_t work)

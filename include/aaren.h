@@ -166,6 +166,27 @@ aaren_status aaren_step(const void *q, const void *k_t, const void *v_t,
                         int64_t S, int64_t H, int64_t d, float scale,
                         aaren_dtype in_dtype, aaren_dtype out_dtype, void *hip_stream);
 
+/* ---- multi-token append -----------------------------------------------------
+ * The same update for T new pairs per (stream, head) in one call: a scan of
+ * the new tokens whose carry-in is the stored state ("Attention as an RNN",
+ * abstract item (4)(ii): new tokens are taken in with constant memory; the
+ * update is the combine of the prefix scan in its method section). The
+ * state is read and written once per call instead of once per token.
+ *   q [H,d];  k, v [T,S,H,d] time-major (k[t] is what aaren_step takes as
+ *   k_t for the t-th new token)  (in_dtype)
+ *   m [S,H], u [S,H], w [S,H,d]  float32, in/out, as for aaren_step
+ *   o [T,S,H,d] (out_dtype) or NULL: o[t] is the output after token t.
+ * Each pair is absorbed with aaren_step's own fp32 arithmetic, so the outputs
+ * and the state equal, bit for bit, those of T aaren_step calls.
+ * T = 0 or S*H = 0: OK, nothing is read or written. No workspace. Errors as
+ * for aaren_step (INVALID_ARG for a negative size or a NULL pointer other
+ * than o, ALIGNMENT for tensors not 16-byte aligned or m, u not 4-byte
+ * aligned, UNSUPPORTED for d or a dtype outside the supported set). */
+aaren_status aaren_append(const void *q, const void *k, const void *v,
+                          float *m, float *u, float *w, void *o,
+                          int64_t S, int64_t T, int64_t H, int64_t d, float scale,
+                          aaren_dtype in_dtype, aaren_dtype out_dtype, void *hip_stream);
+
 /* ---- many-to-one reduction -------------------------------------------------
  * Single-query attention over all N pairs ("Self-attention Does Not Need
  * O(n^2) Memory", sections 1-2; "Attention as an RNN", abstract item (1):

@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("aaren_scan", "aaren_scan_segmented", "aaren_step", "aaren_reduce",
-              "aaren_state_init", "aaren_workspace_clear"):
+              "aaren_state_init", "aaren_workspace_clear", "aaren_append", "aaren_scan_backward"):
         assert n in names
 
 
@@ -114,6 +114,24 @@ def test_step_validation():
     assert L.aaren_state_init(A, A, A + 4, 4, 2, 64, None) == S["align"]
     assert L.aaren_state_init(A, A, A, 4, 2, 48, None) == S["unsup"]
     assert L.aaren_state_init(0, 0, 0, 0, 2, 64, None) == 0
+
+
+def test_append_validation():
+    ap = lambda **kw: L.aaren_append(kw.get("q", A), kw.get("k", A), A, kw.get("m", A),
+                                     kw.get("u", A), kw.get("w", A), kw.get("o", None), 4,
+                                     kw.get("T", 3), 2, kw.get("d", 64), 0.125,
+                                     kw.get("inp", 0), 0, None)
+    assert ap(d=100) == S["unsup"]
+    assert ap(inp=7) == S["unsup"]
+    assert ap(T=-1) == S["arg"]
+    assert ap(m=0) == S["arg"]
+    assert ap(k=0) == S["arg"]
+    assert ap(m=A + 2) == S["align"]
+    assert ap(w=A + 4) == S["align"]
+    assert ap(o=A + 8) == S["align"]
+    # nothing to append: OK without touching anything, even with NULL tensors
+    assert L.aaren_append(0, 0, 0, 0, 0, 0, None, 4, 0, 2, 64, 0.125, 0, 0, None) == 0
+    assert L.aaren_append(0, 0, 0, 0, 0, 0, None, 0, 5, 2, 64, 0.125, 0, 0, None) == 0
 
 
 def test_reduce_validation():

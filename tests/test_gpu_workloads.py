@@ -153,3 +153,32 @@ def test_dense_gradients_in_full():
         bound = (depth * 2.0 ** -24 + 1e-5) * (sds[..., None] * np.abs(kh[:, h])).sum(axis=(0, 1))
         assert np.all(np.abs(host32(dq[h]) - rq[h]) <= bound + 1e-7)
     print(f"dense gradients: dk {e_k:.3e} dv {e_v:.3e}")
+
+
+def test_stream_appends_sampled_streams():
+    """The stream workload's 256 tokens per stream as 16 appends of 16 (the
+    append benchmark's launch shape), on 512 sampled streams."""
+    w = W["stream"]
+    sz = w.sizes
+    S, H, d, T = sz["S"], sz["H"], sz["d"], sz["steps"]
+    block = 16
+    announce(f"workload stream, appends of {block}: {w.describe()}")
+    q, k, v = workloads.step_inputs(S, H, d, T, w.seed, device=dev())
+    scale = workloads.default_scale(d)
+    m, u, ww = aaren.new_state(S, H, d, device=dev())
+    o = torch.empty(block, S, H, d, device=dev())
+    sample = torch.from_numpy(np.sort(np.random.default_rng(6).choice(S, 512, replace=False))).to(dev())
+    kept = []
+    for t0 in range(0, T, block):
+        aaren.aaren_append(q, k[t0:t0 + block], v[t0:t0 + block], m, u, ww, scale, o=o)
+        kept.append(o[:, sample].clone())
+    got = torch.cat(kept)                        # [T, 512, H, d]
+    ks, vs = host32(k[:, sample]), host32(v[:, sample])
+    del k, v
+    st = oracle.state_init(len(sample), H, d)
+    ref = oracle.append(host32(q), ks, vs, st, scale)
+    err = check(got, ref, TOL[torch.float32], "stream appends")
+    L = host32(m[sample]).astype(np.float64) + np.log(host32(u[sample]).astype(np.float64))
+    Lr = st[0] + np.log(st[1])
+    assert np.max(np.abs(L - Lr) / (1 + np.abs(Lr))) <= 1e-5
+    print(f"stream appends: max scaled err over 512 sampled streams x {T} tokens {err:.3e}")

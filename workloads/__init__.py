@@ -37,7 +37,7 @@ import torch
 class Workload:
     """One named workload: its kind, sizes, dtype and seed."""
     name: str
-    kind: str            # "dense" | "segmented" | "step" | "reduce"
+    kind: str            # "dense" | "segmented" | "step" | "append" | "reduce"
     sizes: dict = field(default_factory=dict)
     dtype: str = "f32"   # input dtype: "f32" or "bf16"
     seed: int = 0
@@ -62,6 +62,9 @@ WORKLOADS = {
                        "f32", 4),
     # many independent streams, one token appended per call
     "stream": Workload("stream", "step", dict(S=262144, H=4, d=64, steps=256), "f32", 5),
+    # the same streams and tokens, 16 tokens appended per call
+    "append": Workload("append", "append", dict(S=262144, H=4, d=64, steps=256, block=16), "f32",
+                       5),
     # one query over 2^20 keys
     "reduce": Workload("reduce", "reduce", dict(B=1, H=1, N=1 << 20, d=128), "f32", 6),
 }
