@@ -58,6 +58,8 @@ def _configure(lib):
                                   f64p, opt64, opt64]
     lib.oracle_scan_backward.argtypes = [f32p, f32p, f32p, f32p, i64, i64, i64, i64,
                                          ctypes.c_double, f64p, f64p, f64p]
+    lib.oracle_self_attention.argtypes = [f32p, f32p, f32p, i64, i64, i64, i64, ctypes.c_double,
+                                          ctypes.c_int, i64, i64, f64p, opt64]
     for fn in (lib.oracle_scan, lib.oracle_scan_segmented, lib.oracle_step, lib.oracle_reduce,
                lib.oracle_scan_backward):
         fn.restype = ctypes.c_int
@@ -181,6 +183,23 @@ def scan_backward(q, k, v, dout, scale):
     if rc:
         raise ValueError("oracle_scan_backward rejected its arguments")
     return dq, dk, dv
+
+
+def self_attention(q, k, v, scale, causal: bool = True, rows=None, stats: bool = False):
+    """Self-attention with one query per token: q, k, v [B,H,N,d] -> o
+    [B,H,R,d] float64 for query rows rows = (begin, end) (all rows if None),
+    each the single-query recurrence over pairs 0..i (causal) or all pairs;
+    with stats also L [B,H,R] (log-normaliser, natural units)."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, N, d = k.shape
+    a, b = (0, N) if rows is None else (int(rows[0]), int(rows[1]))
+    o = np.empty((B, H, b - a, d), np.float64)
+    lse = np.empty((B, H, b - a), np.float64) if stats else None
+    rc = _load().oracle_self_attention(q, k, v, B, H, N, d, float(scale), int(bool(causal)), a, b,
+                                       o, _ptr(lse))
+    if rc:
+        raise ValueError("oracle_self_attention rejected its arguments")
+    return (o, lse) if stats else o
 
 
 def max_scaled_err(got, ref) -> float:

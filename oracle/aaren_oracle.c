@@ -41,6 +41,12 @@
  *    weighted by e^{L_i - L_k} <= 1 relative to the current position (L is
  *    non-decreasing along the sequence), then multiplied by p_ii = e^{s_i - L_i}.
  *
+ *  - Self-attention. The memory-efficient-attention review (section 2)
+ *    extends the single-query algorithm to self-attention by computing the
+ *    result of every query in turn, one query per token. Row i here is the
+ *    single-query recurrence for query q_i over pairs 1..i (causal) or over
+ *    all n pairs, so it is the same definition applied n times.
+ *
  * Notation: m = running maximum score, u = scalar accumulator (sum of
  * e^{s_i - m}), w = vector accumulator (sum of e^{s_i - m} v_i). Inputs arrive
  * as float32 (bfloat16 inputs are widened exactly by the caller) and are
@@ -288,5 +294,40 @@ int oracle_scan_backward(const float *q, const float *k, const float *v, const f
             dq[h * d + j] = acc;
         }
     free(dq_unit);
+    return 0;
+}
+
+/* Self-attention, one query per token: q, k, v [B,H,N,d]; rows
+ * row_begin..row_end-1 of every (b,h) are computed, each as the single-query
+ * recurrence of its own query over pairs 0..i (causal != 0) or 0..N-1.
+ * o [B,H,row_end-row_begin,d]; lse_out [B,H,row_end-row_begin] or NULL. */
+int oracle_self_attention(const float *q, const float *k, const float *v,
+                          int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                          int causal, int64_t row_begin, int64_t row_end,
+                          double *o, double *lse_out)
+{
+    if (B < 0 || H < 0 || N < 0 || d < 1 || row_begin < 0 || row_end > N ||
+        row_end < row_begin)
+        return 1;
+    const int64_t rows = row_end - row_begin, units = B * H;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc((size_t)d * sizeof(double));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t job = 0; job < units * rows; ++job) {
+            const int64_t unit = job / rows, i = row_begin + job % rows;
+            const float *qi = q + (unit * N + i) * d;
+            const int64_t last = causal ? i : N - 1;
+            double m = -INFINITY, u = 0.0;
+            memset(w, 0, (size_t)d * sizeof(double));
+            for (int64_t j = 0; j <= last; ++j) {
+                const int64_t row = unit * N + j;
+                absorb(&m, &u, w, d, score(qi, k + row * d, d, scale), v + row * d);
+            }
+            const int64_t out = unit * rows + (i - row_begin);
+            emit(m, u, w, d, o + out * d, NULL, lse_out ? lse_out + out : NULL);
+        }
+        free(w);
+    }
     return 0;
 }

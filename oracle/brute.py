@@ -72,6 +72,16 @@ def sdpa_scan(q, K, V, scale):
     return out[0, 0].numpy()
 
 
+def sdpa_self_attention(Q, K, V, scale, causal):
+    """Self-attention (one query per token) from torch's
+    scaled_dot_product_attention on the CPU in float64: Q, K, V [B,H,n,d]."""
+    import torch
+    Qt, Kt, Vt = (torch.as_tensor(np.asarray(x, np.float64)) for x in (Q, K, V))
+    out = torch.nn.functional.scaled_dot_product_attention(Qt, Kt, Vt, is_causal=bool(causal),
+                                                           scale=float(scale))
+    return out.numpy()
+
+
 def softmax_reduce(q, K, V, scale):
     """Many-to-one output from torch.softmax on the CPU in float64."""
     import torch

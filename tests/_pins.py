@@ -279,6 +279,36 @@ def check_append(orc, seed=25):
     assert empty.shape == (0, S, H, d)
 
 
+def check_self_attention(orc, seed=26):
+    """One query per token: every row equals brute-force attention of its own
+    query over its prefix (causal) or over all pairs, and torch SDPA in
+    float64; with every query equal to q_h the causal rows are the scan and
+    the full rows the reduction; a row range is the slice of the whole."""
+    rng = _rng(seed)
+    B, H, N, d = 2, 3, 37, 8
+    q, k, v = (rng.standard_normal((B, H, N, d)).astype(np.float32) for _ in range(3))
+    k = (1.5 * k).astype(np.float32)
+    scale = 0.4
+    for causal in (True, False):
+        o, lse = orc.self_attention(q, k, v, scale, causal=causal, stats=True)
+        _close(o, brute.sdpa_self_attention(q, k, v, scale, causal), 1e-12, "vs torch SDPA")
+        for b, h, i in ((0, 0, 0), (1, 2, N - 1), (0, 1, 17), (1, 0, 5)):
+            last = i + 1 if causal else N
+            _close(o[b, h, i], brute.attend(q[b, h, i], k[b, h, :last], v[b, h, :last], scale),
+                   1e-12, "vs brute force")
+            _close(lse[b, h, i], brute.log_normaliser(q[b, h, i], k[b, h, :last], scale), 1e-13,
+                   "self-attention log-normaliser")
+        part = orc.self_attention(q, k, v, scale, causal=causal, rows=(10, 23))
+        _close(part, o[:, :, 10:23], 1e-15, "row range")
+    qh = rng.standard_normal((H, d)).astype(np.float32)
+    same = np.ascontiguousarray(np.broadcast_to(qh[None, :, None, :], (B, H, N, d)))
+    _close(orc.self_attention(same, k, v, scale, causal=True), orc.scan(qh, k, v, scale), 1e-13,
+           "equal queries, causal == scan")
+    full = orc.self_attention(same, k, v, scale, causal=False)
+    _close(full, np.broadcast_to(orc.reduce(qh, k, v, scale)[:, :, None, :], full.shape), 1e-13,
+           "equal queries, all pairs == reduce")
+
+
 def check_segmented(orc, seed=21):
     """Each packed sequence is scanned on its own: == brute force per segment;
     empty and length-1 segments included."""
@@ -383,5 +413,5 @@ def check_backward_closed_forms(orc, seed=24):
 
 ALL = [check_golden, check_scan_vs_definition, check_stats, check_single_token,
        check_running_mean, check_two_tokens, check_dominating_key, check_shift_invariance,
-       check_convex_hull, check_bracketing, check_reduce, check_step, check_append, check_segmented,
+       check_convex_hull, check_bracketing, check_reduce, check_step, check_append, check_self_attention, check_segmented,
        check_backward, check_backward_finite_differences, check_backward_closed_forms]

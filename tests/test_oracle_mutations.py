@@ -66,6 +66,14 @@ MUTATIONS = [
      "dk[row * d + j] = scale * ds * (double)k[row * d + j];"),
     ("backward: dq of the first batch row only", "oracle_scan_backward",
      "for (int64_t b = 0; b < B; ++b)", "for (int64_t b = 0; b < 1; ++b)"),
+    ("self-attention: causal rows exclude their own pair", "oracle_self_attention",
+     "for (int64_t j = 0; j <= last; ++j)", "for (int64_t j = 0; j < (last > 0 ? last : 1); ++j)"),
+    ("self-attention: the first query for every row", "oracle_self_attention",
+     "const float *qi = q + (unit * N + i) * d;", "const float *qi = q + (unit * N) * d;"),
+    ("self-attention: all pairs but the last", "oracle_self_attention",
+     "const int64_t last = causal ? i : N - 1;", "const int64_t last = causal ? i : (N > 1 ? N - 2 : 0);"),
+    ("self-attention: keys of the wrong head", "oracle_self_attention",
+     "const int64_t row = unit * N + j;", "const int64_t row = (unit / H) * H * N + j;"),
 ]
 
 
