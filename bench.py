@@ -12,6 +12,9 @@ already resident in HBM:
   append                   : aaren_state_init + 16 aaren_append calls of 16
                              tokens, the same 256 tokens per stream
   backward                 : one aaren_scan_backward call on the dense batch
+  self_attn                : one aaren_self_attention call (causal, one query
+                             per token; matrix cores: TFLOP/s against the bf16
+                             peak)
   reduce                   : one aaren_reduce call         (keys = B*H*N)
 W untimed steps, then exactly K steps between two HIP events recorded on the
 stream the kernels run on. Prints one JSON line. The default workload is the
@@ -41,6 +44,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD's published figure
 # Steps rotate over enough copies of the inputs and outputs that one pass over
 # them moves at least this many bytes: eight times the 256 MB Infinity Cache,
 # so a step's data comes from HBM and not from what the previous step left in
@@ -56,6 +60,7 @@ KERNEL_SOURCES = {
     "backward": ["scan_backward.hip", "lookback.h", "device.h", "layout.h"],
     "step": ["step.hip", "device.h", "layout.h"],
     "append": ["step.hip", "device.h", "layout.h"],
+    "self_attention": ["self_attention.hip", "self_attention.h", "device.h", "layout.h"],
     "reduce": ["reduce.hip", "device.h", "layout.h"],
 }
 
@@ -329,6 +334,44 @@ def make(name: str, device):
                                              f"tokens in appends of {blk}")
         b.cpu = cpu
 
+    elif w.kind == "self_attention":
+        B, H, N, d, causal = z["B"], z["H"], z["N"], z["d"], bool(z["causal"])
+        q, k, v = wl.self_attention_inputs(B, H, N, d, w.seed, device=device)
+        scale = wl.default_scale(d)
+        o = torch.empty(B, H, N, d, device=device)
+        ws = torch.empty(aaren.aaren_self_attention_workspace_size(B, H, N, d), dtype=torch.uint8,
+                         device=device)
+        b.step = lambda: aaren.aaren_self_attention(q, k, v, scale, causal=causal, out=o,
+                                                    workspace=ws)
+        b.kind = "self_attention"
+        b.unit = "TFLOP/s"
+        b.bound = "mfma"
+        # algorithmic flops: 2d for q.k and 2d for p.v per (query, key) pair
+        pairs = N * (N + 1) // 2 if causal else N * N
+        b.flops_per_launch = 4 * d * pairs * B * H
+        b.units = b.flops_per_launch / 1e12
+        b.bytes_per_launch = 3 * q.numel() * 2 + o.numel() * 4
+        b.config = {"workload": f"self-attention, one query per token {b.describe}", "B": B, "H": H,
+                    "N": N, "d": d, "causal": causal, "in_dtype": "bf16", "out_dtype": "f32",
+                    "flops_per_call": b.flops_per_launch}
+        b.kernel = "self_attention_kernel (+ attn_transpose_kernel)"
+
+        def cpu(budget_s):
+            import oracle
+            rows = 256
+            qh, kh, vh = (t[:1, :1].float().cpu().numpy() for t in (q, k, v))
+            done, t0 = 0, time.perf_counter()
+            while True:
+                oracle.self_attention(qh, kh, vh, scale, causal=causal, rows=(N - rows, N))
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            per = sum(4 * d * ((i + 1) if causal else N) for i in range(N - rows, N))
+            return done * per / dt / 1e12, (f"{done} pass(es) over the last {rows} query rows of "
+                                            f"one head (N={N}, d={d})")
+        b.cpu = cpu
+
     else:  # reduce
         B, H, N, d = z["B"], z["H"], z["N"], z["d"]
         q, k, v = wl.reduce_inputs(B, H, N, d, w.seed, device=device)
@@ -375,7 +418,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
                     choices=["single", "dense", "long_bf16", "ragged", "stream", "append",
-                             "reduce", "backward", "copy"])
+                             "reduce", "backward", "self_attn", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle time budget for cpu_baseline (0 to skip)")
     args = ap.parse_args()
@@ -405,6 +448,15 @@ def main():
     launch_s = ms / 1e3 / b.launches_per_step
     achieved = b.bytes_per_launch / launch_s / 1e9
     traffic = measured_traffic(b.kind, args.workload) if b.kind != "copy" else None
+    if getattr(b, "bound", "hbm") == "mfma":
+        tflops = b.flops_per_launch / launch_s / 1e12
+        roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                    "kernel": b.kernel, "algorithmic_flops_per_launch": b.flops_per_launch}
+    else:
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                    "kernel": b.kernel, "algorithmic_bytes_per_launch": b.bytes_per_launch}
 
     cpu = None
     if args.cpu_seconds > 0 and b.cpu is not None:
@@ -432,9 +484,7 @@ def main():
                              if b.sets > 1 else "one input set")),
         "achieved_GBps": achieved,
         "peak_frac": achieved / PEAK_HBM_GBS,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": b.kernel, "algorithmic_bytes_per_launch": b.bytes_per_launch},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

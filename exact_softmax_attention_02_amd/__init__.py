@@ -31,6 +31,7 @@ EXPORTS = (
     "aaren_scan_workspace_size", "aaren_scan", "aaren_scan_segmented_workspace_size",
     "aaren_scan_segmented", "aaren_state_init", "aaren_step", "aaren_reduce_workspace_size",
     "aaren_reduce", "aaren_scan_backward_workspace_size", "aaren_scan_backward", "aaren_append",
+    "aaren_self_attention_workspace_size", "aaren_self_attention",
 )
 
 
@@ -60,6 +61,8 @@ def _load():
         "aaren_state_init": (I, [P, P, P, I64, I64, I64, P]),
         "aaren_step": (I, [P, P, P, P, P, P, P, I64, I64, I64, F, I, I, P]),
         "aaren_append": (I, [P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P]),
+        "aaren_self_attention_workspace_size": (SZ, [I64, I64, I64, I64]),
+        "aaren_self_attention": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, I, P, SZ, P]),
         "aaren_reduce_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_reduce": (I, [P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
         "aaren_scan_backward_workspace_size": (SZ, [I64, I64, I64, I64]),
@@ -314,6 +317,33 @@ def aaren_append(q, k, v, m, u, w, scale=None, out_dtype=None, o=None, emit=True
                             default_scale(d) if scale is None else float(scale),
                             _dtype_code(k.dtype), _dtype_code(out_dtype), _stream(dev)))
     return o if emit else None
+
+
+def aaren_self_attention_workspace_size(B, H, N, d) -> int:
+    return int(lib.aaren_self_attention_workspace_size(B, H, N, d))
+
+
+def aaren_self_attention(q, k, v, scale=None, causal=True, out_dtype=None, out=None, lse=None,
+                         return_lse=False, workspace=None):
+    """Self-attention, one query per token: q, k, v [B,H,N,d] bfloat16 -> o
+    [B,H,N,d] (and lse [B,H,N] float32 with return_lse or a given lse)."""
+    dev = _need_cuda(q, k, v, out, lse, workspace)
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("expected q, k, v [B,H,N,d] of one dtype")
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty(B, H, N, d, dtype=out_dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    need = aaren_self_attention_workspace_size(B, H, N, d)
+    ws = workspace if workspace is not None else _workspace("attn", need, dev, False)
+    _check(lib.aaren_self_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                    default_scale(d) if scale is None else float(scale),
+                                    int(bool(causal)), _dtype_code(q.dtype), _dtype_code(out.dtype),
+                                    _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(dev)))
+    return (out, lse) if (return_lse or lse is not None) else out
 
 
 def aaren_reduce(q, k, v, scale=None, out_dtype=None, stats=False, out=None, workspace=None):

@@ -9,6 +9,7 @@
 #include <unordered_map>
 
 #include "layout.h"
+#include "self_attention.h"
 
 #define AAREN_API extern "C" __attribute__((visibility("default")))
 
@@ -577,6 +578,72 @@ AAREN_API aaren_status aaren_append(const void *q, const void *k, const void *v,
     return hip_status(aaren::launch_append(p, (int)d, in_dtype, out_dtype,
                                            static_cast<hipStream_t>(hip_stream)),
                       "append launch");
+}
+
+// ---- self-attention, one query per token -----------------------------------------
+
+AAREN_API size_t aaren_self_attention_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d)
+{
+    if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128))
+        return 0;
+    const int64_t elems = mul_checked({B, H, d, aaren::attn_padded_keys(N)});
+    if (elems < 0)
+        return 0;
+    return aaren::round256((size_t)elems * 2);
+}
+
+AAREN_API aaren_status aaren_self_attention(const void *q, const void *k, const void *v, void *o,
+                                            float *lse, int64_t B, int64_t H, int64_t N,
+                                            int64_t d, float scale, int causal,
+                                            aaren_dtype in_dtype, aaren_dtype out_dtype,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *hip_stream)
+{
+    if (B < 0 || H < 0 || N < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
+                    (long long)B, (long long)H, (long long)N);
+    CHECK(check_common(d, in_dtype, out_dtype));
+    if (in_dtype != AAREN_BF16)
+        return fail(AAREN_ERR_UNSUPPORTED, "self-attention takes bfloat16 q, k, v");
+    const int64_t elems = mul_checked({B, H, N, d});
+    if (elems < 0 || mul_checked({B, H, d, aaren::attn_padded_keys(N)}) < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "B*H*N*d overflows");
+    if (elems == 0)
+        return AAREN_OK;
+    const int64_t blocks = B * H * ((N + aaren::kAttnQueries - 1) / aaren::kAttnQueries);
+    if (blocks > 0x7fffffffLL || B * H > 65535)
+        return fail(AAREN_ERR_UNSUPPORTED, "B*H = %lld or %lld query tiles exceed the launch limits",
+                    (long long)(B * H), (long long)blocks);
+    CHECK(check_ptr(q, "q"));
+    CHECK(check_ptr(k, "k"));
+    CHECK(check_ptr(v, "v"));
+    CHECK(check_ptr(o, "o"));
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(AAREN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
+    const size_t need = aaren_self_attention_workspace_size(B, H, N, d);
+    if (!workspace || workspace_bytes < need)
+        return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    need);
+    if (!aligned16(workspace))
+        return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+    aaren::AttnParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.vt = static_cast<uint16_t *>(workspace);
+    p.o = o;
+    p.lse = lse;
+    p.bh = B * H;
+    p.N = N;
+    p.Np = aaren::attn_padded_keys(N);
+    p.qscale = scale * 1.44269504088896340736f;
+    p.causal = causal ? 1 : 0;
+    if (log_enabled())
+        fprintf(stderr, "[aaren] self_attention B=%lld H=%lld N=%lld d=%lld causal=%d\n",
+                (long long)B, (long long)H, (long long)N, (long long)d, p.causal);
+    return hip_status(aaren::launch_self_attention(p, (int)d, out_dtype,
+                                                   static_cast<hipStream_t>(hip_stream)),
+                      "self-attention launch");
 }
 
 // ---- many-to-one reduction ------------------------------------------------------

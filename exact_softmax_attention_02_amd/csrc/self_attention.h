@@ -1,0 +1,44 @@
+// Parameters and launcher of the self-attention kernels (one query per token).
+// Nothing here is part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "aaren.h"
+
+namespace aaren {
+
+// Tile shapes: a workgroup of kAttnWaves waves takes 32 queries per wave; keys
+// and values go through LDS 64 at a time.
+constexpr int kAttnWaves = 4;
+constexpr int kAttnQueries = 32 * kAttnWaves;
+constexpr int kAttnKeys = 64;
+
+// Rows of the transposed-value workspace are padded to a whole number of key
+// tiles (the padding holds zeros).
+__host__ __device__ constexpr int64_t attn_padded_keys(int64_t N)
+{
+    return (N + kAttnKeys - 1) / kAttnKeys * kAttnKeys;
+}
+
+struct AttnParams {
+    const uint16_t *q;   // bf16 bits [BH][N][D]
+    const uint16_t *k;   // bf16 bits [BH][N][D]
+    const uint16_t *v;   // bf16 bits [BH][N][D]
+    uint16_t *vt;        // workspace: bf16 bits [BH][D][Np], V transposed, zero past N
+    void *o;             // [BH][N][D], float or bf16
+    float *lse;          // [BH][N] or null, natural units
+    int64_t bh;          // B*H
+    int64_t N;
+    int64_t Np;          // attn_padded_keys(N)
+    float qscale;        // scale * log2(e)
+    int causal;
+};
+
+hipError_t launch_self_attention(const AttnParams &p, int D, aaren_dtype out_dtype,
+                                 hipStream_t stream);
+
+}  // namespace aaren

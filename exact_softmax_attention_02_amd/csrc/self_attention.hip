@@ -1,0 +1,306 @@
+// Self-attention with one query per token, on the matrix cores.
+//
+// The memory-efficient-attention review (section 2) extends the single-query
+// algorithm to self-attention by evaluating every query in turn with the same
+// constant-memory recurrence; its GPU/TPU section (body lost) and its
+// introduction mention chunking. Here each workgroup carries 128 queries
+// through the keys 64 at a time with the same running-maximum combine as the
+// single-query path: per key tile, S = scale K Q^T on the bf16 matrix cores,
+// the new running maximum per query, P = e^{S - m}, and O += P V; the
+// normaliser is divided out at the end. Causal: query i attends to keys 0..i.
+//
+// Layout choices (gfx950, wave64, v_mfma_f32_32x32x16_bf16: lane l holds 8
+// consecutive k of row l%32 of A and of column l%32 of B; accumulator
+// register r of lane l is row 8(r/4) + 4(l/32) + r%4, column l%32):
+//  * Scores are computed transposed, S^T = K Q^T, so a query is a column: a
+//    lane owns one query (l%32) and 16 keys per 32-key block, and the row
+//    maximum and sum need one exchange between the two half-waves.
+//  * The K rows feeding the A operand are permuted (row m of the MFMA reads
+//    key kappa(m)) so that accumulator registers 8s..8s+7 of a lane hold 8
+//    consecutive keys: they are then directly the B operand of
+//    O^T += V^T P^T for that 16-key step, with no data movement.
+//  * V^T must present 8 consecutive keys of one dimension per lane; V is
+//    transposed once into the workspace by a pre-pass, so its tiles load
+//    into LDS as plain rows.
+//  * P is carried to ~15 significant bits as bf16 hi + bf16 lo (two MFMAs per
+//    step): rounding P to bf16 alone would move outputs by up to ~2^-9 |v|,
+//    the whole budget of the bf16 tolerance. The normaliser sums P in fp32.
+#include <type_traits>
+
+#include "device.h"
+#include "self_attention.h"
+
+namespace aaren {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(1))) void *gptr;
+typedef __attribute__((address_space(3))) void *lptr;
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
+}
+
+// V [BH][N][D] -> V^T [BH][D][Np], zero for keys N..Np-1. One workgroup per
+// 64 keys x 64 dimensions.
+template <int D>
+__global__ __launch_bounds__(256) void attn_transpose_kernel(const AttnParams p)
+{
+    __shared__ uint16_t t[64][64 + 2];  // [key][dim]
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.z, key0 = (int64_t)blockIdx.x * 64, dim0 = blockIdx.y * 64;
+    for (int c = tid; c < 512; c += 256) {
+        const int key = c / 8, ch = c % 8;
+        u32x4 x = {0, 0, 0, 0};
+        if (key0 + key < p.N)
+            x = load16(p.v + ((bh * p.N + key0 + key) * D + dim0 + 8 * ch));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            t[key][8 * ch + 2 * e] = (uint16_t)(x[e] & 0xffffu);
+            t[key][8 * ch + 2 * e + 1] = (uint16_t)(x[e] >> 16);
+        }
+    }
+    __syncthreads();
+    for (int c = tid; c < 512; c += 256) {
+        const int dim = c / 8, kc = c % 8;
+        u32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            y[e] = (uint32_t)t[8 * kc + 2 * e][dim] | ((uint32_t)t[8 * kc + 2 * e + 1][dim] << 16);
+        store16(p.vt + ((bh * D + dim0 + dim) * p.Np + key0 + 8 * kc), y);
+    }
+}
+
+template <typename Tout>
+__device__ __forceinline__ void store4(Tout *dst, float a, float b, float c, float d)
+{
+    if constexpr (sizeof(Tout) == 4) {
+        store16(dst, u32x4{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c),
+                           __float_as_uint(d)});
+    } else {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2 *>(dst) =
+            u32x2{bf16_bits(a) | (bf16_bits(b) << 16), bf16_bits(c) | (bf16_bits(d) << 16)};
+    }
+}
+
+template <int D, typename Tout>
+__global__ __launch_bounds__(64 * kAttnWaves, 8 / kAttnWaves) void self_attention_kernel(const AttnParams p)
+{
+    constexpr int KS = D / 16;          // 16-wide k-steps of S^T = K Q^T
+    constexpr int DT = D / 32;          // 32-row tiles of O^T
+    constexpr int KC = D / (8 * kAttnWaves);  // 1 KB copies per wave per tile (K and V^T each)
+    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kAttnKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * kAttnKeys];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int h32 = lane >> 5, l32 = lane & 31;
+    // workgroups of one head are adjacent (they share its keys in the caches);
+    // within a head the longest causal rows go first
+    const int64_t nqt = (p.N + kAttnQueries - 1) / kAttnQueries;
+    const int64_t bh = blockIdx.x / nqt;
+    const int64_t q0 = (nqt - 1 - (int64_t)(blockIdx.x % nqt)) * kAttnQueries;
+    const int64_t qi = q0 + 32 * wave + l32;  // this lane's query
+
+    // a negative scale is moved into q (flipping a bf16 sign is exact), so the
+    // scores' scale c2 below is never negative and a maximum of raw scores is
+    // the maximum of scaled ones
+    const uint32_t qflip = p.qscale < 0.f ? 0x80008000u : 0u;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        u32x4 x = {0, 0, 0, 0};
+        if (qi < p.N)
+            x = load16(p.q + ((bh * p.N + qi) * D + 16 * kk + 8 * h32)) ^ qflip;
+        qf[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+
+    const int64_t kend = (p.causal && q0 + kAttnQueries < p.N) ? q0 + kAttnQueries : p.N;
+    const int ntiles = (int)((kend + kAttnKeys - 1) / kAttnKeys);
+
+    // Tiles go from global memory straight into LDS (global_load_lds: lane i
+    // of a wave writes 16 bytes at base + 16 i). Rows are unpadded; the
+    // 16-byte chunks of a row are stored XOR-swizzled so that the fragment
+    // reads below (16 lanes, 16 different rows, one chunk column) hit 16
+    // different bank groups: K row r (D/8 chunks) keeps chunk c at position
+    // c ^ kswz(r); a V^T row (8 chunks of 8 keys) at c ^ vswz(r).
+    auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+    auto vswz = [](int r) { return (r >> 1) & 7; };
+    constexpr int KRPI = 1024 / (2 * D);  // K rows per 1 KB copy
+    const uint16_t *kh = p.k + bh * p.N * D;
+    const uint16_t *vth = p.vt + bh * D * p.Np;
+    auto load_tile = [&](int j, int buf) {
+        const int64_t k0 = (int64_t)j * kAttnKeys;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const int blk = kAttnWaves * c + wave;  // 1 KB block of the tile this copy fills
+            const int row = blk * KRPI + lane / (D / 8), pos = lane % (D / 8);
+            int64_t key = k0 + row;
+            key = key < p.N ? key : p.N - 1;  // rows past N: a real row, masked later
+            __builtin_amdgcn_global_load_lds(
+                (gptr)(kh + key * D + 8 * (pos ^ kswz(row))), (lptr)(&sk[buf][blk * 512]), 16, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const int blk = kAttnWaves * c + wave;
+            const int row = blk * 8 + lane / 8, pos = lane % 8;
+            __builtin_amdgcn_global_load_lds(
+                (gptr)(vth + row * p.Np + k0 + 8 * (pos ^ vswz(row))), (lptr)(&sv[buf][blk * 512]),
+                16, 0, 0);
+        }
+    };
+
+    load_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        oacc[dt] = f32x16{};
+    float m = kNegInf, lsum = 0.f;  // m in log2 units; lsum: this half-wave's keys only
+
+    // A-operand row m = l32 of each 32-key block reads key kappa(m)
+    const int krow = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+    // scores are scaled inside the exponent: e^{c2 s - m}
+    const float c2 = fabsf(p.qscale);
+
+    // One key tile. EDGE: the tile holds keys past N or past some query of
+    // this workgroup (causal); keys at offset >= lim from the tile's first key
+    // are then masked for this lane's query (excluded from the maximum, weight
+    // exactly 0).
+    auto tile = [&](int buf, int lim, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        f32x16 s[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            s[t] = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+                s[t] = mfma32(load16(&sk[buf][(32 * t + krow) * D +
+                                              8 * ((2 * kk + h32) ^ kswz(32 * t + krow))]),
+                              qf[kk], s[t]);
+        }
+        auto key_off = [&](int t, int r) { return 32 * t + 16 * (r >> 3) + 8 * h32 + (r & 7); };
+        float tx = kNegInf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                tx = fmaxf(tx, (!EDGE || key_off(t, r) < lim) ? s[t][r] : kNegInf);
+        tx = fmaxf(tx, __shfl_xor(tx, 32));
+        // a lane whose keys are all masked has tx = -inf; with a zero scale
+        // tx * c2 is NaN, and fmaxf keeps m
+        const float mnew = fmaxf(m, tx * c2);
+        const float alpha = exp2_fast(m - mnew);  // 0 on the first tile (m = -inf)
+        m = mnew;
+        lsum *= alpha;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                oacc[dt] *= alpha;
+        }
+        // O^T += V^T P^T, 16 keys per step, P as bf16 hi + lo
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                f32x8 pe;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pe[e] = exp2_fast(__builtin_fmaf(s[t][8 * s2 + e], c2, -mnew));
+                    if (EDGE && key_off(t, 8 * s2 + e) >= lim)
+                        pe[e] = 0.f;
+                    lsum += pe[e];
+                }
+                // hi: the upper 16 bits of each float (truncation, error < 2^-7 p);
+                // lo: the remainder rounded to bf16, so hi + lo is within 2^-15 p
+                u32x4 hp;
+                f32x8 hf;
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const uint32_t a = __float_as_uint(pe[e]), b = __float_as_uint(pe[e + 1]);
+                    hp[e / 2] = (a >> 16) | (b & 0xffff0000u);
+                    hf[e] = __uint_as_float(a & 0xffff0000u);
+                    hf[e + 1] = __uint_as_float(b & 0xffff0000u);
+                }
+                const bf16x8 ph = __builtin_bit_cast(bf16x8, hp);
+                const bf16x8 pl = __builtin_convertvector(pe - hf, bf16x8);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int vr = 32 * dt + l32;
+                    const u32x4 a = load16(&sv[buf][vr * kAttnKeys +
+                                                    8 * ((4 * t + 2 * s2 + h32) ^ vswz(vr))]);
+                    oacc[dt] = mfma32(a, ph, oacc[dt]);
+                    oacc[dt] = mfma32(a, pl, oacc[dt]);
+                }
+            }
+        }
+    };
+
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < ntiles)
+            load_tile(j + 1, buf ^ 1);  // that buffer was last read before the previous barrier
+        const int64_t k0 = (int64_t)j * kAttnKeys;
+        if (k0 + kAttnKeys > p.N || (p.causal && k0 + kAttnKeys - 1 > q0)) {
+            int64_t lim = p.N - k0;
+            if (p.causal && qi + 1 - k0 < lim)
+                lim = qi + 1 - k0;
+            tile(buf, lim < 0 ? 0 : (lim > kAttnKeys ? kAttnKeys : (int)lim),
+                 std::integral_constant<bool, true>{});
+        } else {
+            tile(buf, kAttnKeys, std::integral_constant<bool, false>{});
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
+        __syncthreads();
+    }
+
+    lsum += __shfl_xor(lsum, 32);
+    if (qi < p.N) {
+        const float inv = 1.f / lsum;
+        Tout *orow = static_cast<Tout *>(p.o) + (bh * p.N + qi) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                store4<Tout>(orow + 32 * dt + 8 * g + 4 * h32, oacc[dt][4 * g] * inv,
+                             oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
+                             oacc[dt][4 * g + 3] * inv);
+        }
+        if (p.lse && h32 == 0)
+            p.lse[bh * p.N + qi] = (m + log2_fast(lsum)) * kLn2;
+    }
+}
+
+template <int D>
+static hipError_t attention_one(const AttnParams &p, aaren_dtype out, hipStream_t stream)
+{
+    hipLaunchKernelGGL((attn_transpose_kernel<D>),
+                       dim3((unsigned)(p.Np / 64), (unsigned)(D / 64), (unsigned)p.bh), dim3(256),
+                       0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t blocks = p.bh * ((p.N + kAttnQueries - 1) / kAttnQueries);
+    if (out == AAREN_F32)
+        hipLaunchKernelGGL((self_attention_kernel<D, float>), dim3((unsigned)blocks),
+                           dim3(64 * kAttnWaves), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((self_attention_kernel<D, bf16>), dim3((unsigned)blocks),
+                           dim3(64 * kAttnWaves), 0,
+                           stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_self_attention(const AttnParams &p, int D, aaren_dtype out_dtype,
+                                 hipStream_t stream)
+{
+    return D == 64 ? attention_one<64>(p, out_dtype, stream)
+                   : attention_one<128>(p, out_dtype, stream);
+}
+
+}  // namespace aaren

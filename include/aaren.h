@@ -204,6 +204,28 @@ aaren_status aaren_reduce(const void *q, const void *k, const void *v, void *o,
                           aaren_dtype in_dtype, aaren_dtype out_dtype,
                           void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* ---- self-attention, one query per token ------------------------------------
+ * "Self-attention Does Not Need O(n^2) Memory", section 2: the single-query
+ * algorithm extended to self-attention by evaluating every query with the
+ * same recurrence (and the review's chunked GPU/TPU implementation, section
+ * 4, whose body is lost). Row i of each (b,h) is the attention of query q_i
+ * over pairs 0..i (causal != 0) or over all N pairs:
+ *   q, k, v [B,H,N,d] bfloat16 (in_dtype must be AAREN_BF16);
+ *   o [B,H,N,d] (out_dtype F32 or BF16);
+ *   lse [B,H,N] float32 or NULL: L_i = ln sum_j e^{s_ij} (natural units).
+ * Scores and the value sums are accumulated in fp32 on the matrix cores;
+ * the softmax weights enter the value sum with 16 significant bits.
+ * The workspace (size from the query; no zero-fill needed, every call
+ * overwrites what it reads) holds V transposed. B*H*N = 0: OK, nothing
+ * is read or written. Statuses as for aaren_scan; UNSUPPORTED also for
+ * float32 inputs and for B*H > 65535. */
+size_t aaren_self_attention_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d);
+aaren_status aaren_self_attention(const void *q, const void *k, const void *v, void *o,
+                                  float *lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                                  float scale, int causal, aaren_dtype in_dtype,
+                                  aaren_dtype out_dtype, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -134,6 +134,25 @@ def test_append_validation():
     assert L.aaren_append(0, 0, 0, 0, 0, 0, None, 0, 5, 2, 64, 0.125, 0, 0, None) == 0
 
 
+def test_self_attention_validation():
+    sa = lambda **kw: L.aaren_self_attention(A, A, A, kw.get("o", A), kw.get("lse", None), 1, 2,
+                                             kw.get("N", 100), kw.get("d", 64), 0.125, 1,
+                                             kw.get("inp", 1), 0, kw.get("ws", A),
+                                             kw.get("wsb", 1 << 20), None)
+    assert sa(inp=0) == S["unsup"]           # float32 inputs: bf16 only
+    assert sa(d=96) == S["unsup"]
+    assert sa(N=-1) == S["arg"]
+    assert sa(o=0) == S["arg"]
+    assert sa(o=A + 4) == S["align"]
+    assert sa(lse=A + 2) == S["align"]
+    assert sa(wsb=16) == S["ws"]
+    assert sa(ws=A + 8) == S["align"]
+    assert L.aaren_self_attention(0, 0, 0, 0, None, 1, 2, 0, 64, 0.125, 1, 1, 0, 0, 0, None) == 0
+    # V transposed, keys padded to a multiple of 64, bf16
+    assert aaren.aaren_self_attention_workspace_size(2, 3, 100, 64) == 2 * 3 * 64 * 128 * 2
+    assert aaren.aaren_self_attention_workspace_size(1, 1, 10, 100) == 0
+
+
 def test_reduce_validation():
     rd = lambda **kw: L.aaren_reduce(A, A, A, A, kw.get("m", None), None, 1, 1, kw.get("N", 10),
                                      64, 0.125, 0, 0, kw.get("ws", A), kw.get("wsb", 1 << 20), None)

@@ -182,3 +182,25 @@ def test_stream_appends_sampled_streams():
     Lr = st[0] + np.log(st[1])
     assert np.max(np.abs(L - Lr) / (1 + np.abs(Lr))) <= 1e-5
     print(f"stream appends: max scaled err over 512 sampled streams x {T} tokens {err:.3e}")
+
+
+def test_self_attention_sampled_rows():
+    """The causal self-attention workload at full size (the benchmark's call),
+    rows at the start, the middle and the end of every (b,h) against the
+    oracle's rows."""
+    w = W["self_attn"]
+    sz = w.sizes
+    B, H, N, d = sz["B"], sz["H"], sz["N"], sz["d"]
+    announce(f"workload self_attn: {w.describe()}")
+    q, k, v = workloads.self_attention_inputs(B, H, N, d, w.seed, device=dev())
+    scale = workloads.default_scale(d)
+    o, lse = aaren.aaren_self_attention(q, k, v, scale, causal=bool(sz["causal"]), return_lse=True)
+    torch.cuda.synchronize()
+    qh, kh, vh = host32(q), host32(k), host32(v)
+    worst = 0.0
+    for a, b in ((0, 128), (N // 2 - 64, N // 2 + 64), (N - 128, N)):
+        ref, rl = oracle.self_attention(qh, kh, vh, scale, causal=bool(sz["causal"]), rows=(a, b),
+                                        stats=True)
+        worst = max(worst, check(o[:, :, a:b], ref, TOL[torch.bfloat16], f"rows {a}..{b}"))
+        assert oracle.max_scaled_err(host32(lse[:, :, a:b]), rl) <= 1e-5
+    print(f"self_attn: max scaled err over 384 rows x {B * H} heads {worst:.3e}")

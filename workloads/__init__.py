@@ -37,7 +37,7 @@ import torch
 class Workload:
     """One named workload: its kind, sizes, dtype and seed."""
     name: str
-    kind: str            # "dense" | "segmented" | "step" | "append" | "reduce"
+    kind: str            # "dense" | "segmented" | "step" | "append" | "self_attention" | "reduce"
     sizes: dict = field(default_factory=dict)
     dtype: str = "f32"   # input dtype: "f32" or "bf16"
     seed: int = 0
@@ -65,6 +65,9 @@ WORKLOADS = {
     # the same streams and tokens, 16 tokens appended per call
     "append": Workload("append", "append", dict(S=262144, H=4, d=64, steps=256, block=16), "f32",
                        5),
+    # self-attention, one query per token, causal, at the pages' sequence length
+    "self_attn": Workload("self_attn", "self_attention", dict(B=2, H=16, N=16384, d=128, causal=1),
+                          "bf16", 7),
     # one query over 2^20 keys
     "reduce": Workload("reduce", "reduce", dict(B=1, H=1, N=1 << 20, d=128), "f32", 6),
 }
@@ -138,6 +141,16 @@ def step_inputs(S, H, d, steps, seed, device="cpu", dtype="f32"):
     q = torch.randn(H, d, generator=g, device=device, dtype=torch.float32)
     k = torch.randn(steps, S, H, d, generator=g, device=device, dtype=torch.float32)
     v = torch.randn(steps, S, H, d, generator=g, device=device, dtype=torch.float32)
+    td = _torch_dtype(dtype)
+    return q.to(td).contiguous(), k.to(td).contiguous(), v.to(td).contiguous()
+
+
+def self_attention_inputs(B, H, N, d, seed, device="cpu", dtype="bf16"):
+    """Q, K, V [B,H,N,d] N(0,1), one query per token."""
+    g = _gen(seed, device)
+    q = torch.randn(B, H, N, d, generator=g, device=device, dtype=torch.float32)
+    k = torch.randn(B, H, N, d, generator=g, device=device, dtype=torch.float32)
+    v = torch.randn(B, H, N, d, generator=g, device=device, dtype=torch.float32)
     td = _torch_dtype(dtype)
     return q.to(td).contiguous(), k.to(td).contiguous(), v.to(td).contiguous()
 
