@@ -202,6 +202,31 @@ def self_attention(q, k, v, scale, causal: bool = True, rows=None, stats: bool =
     return (o, lse) if stats else o
 
 
+def bf16_round(a):
+    """Round float64 values to the nearest bfloat16 value (8 significant
+    bits), ties to even; returned as float64. Normal range only."""
+    a = np.asarray(a, np.float64)
+    m, e = np.frexp(a)                       # a = m 2^e, 1/2 <= |m| < 1
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def layer_forward(x, w_kv, q, scale, out_bf16: bool = True):
+    """One Aaren layer: x [B,N,Dm], w_kv [Dm, 2*H*d] (W_K | W_V), q [H,d]
+    -> o [B,N,H,d] float64. [K | V] = x w_kv in float64, stored as float32
+    (the layer keeps K and V in fp32), then the many-to-many scan of q_h over
+    each (b, h) ("Attention as an RNN" review, proposed method: a learned
+    query, the prefix-scan output); with out_bf16 the output is rounded to
+    bfloat16, the precision a stacked layer receives."""
+    x, w_kv, q = (np.asarray(t, np.float64) for t in (x, w_kv, q))
+    B, N, Dm = x.shape
+    H, d = q.shape
+    kv = (x.reshape(B * N, Dm) @ w_kv).reshape(B, N, 2, H, d).astype(np.float32)
+    k = np.ascontiguousarray(kv[:, :, 0].transpose(0, 2, 1, 3))   # [B,H,N,d]
+    v = np.ascontiguousarray(kv[:, :, 1].transpose(0, 2, 1, 3))
+    o = scan(q.astype(np.float32), k, v, scale).transpose(0, 2, 1, 3)  # [B,N,H,d]
+    return bf16_round(o) if out_bf16 else np.ascontiguousarray(o)
+
+
 def max_scaled_err(got, ref) -> float:
     """max over elements of |got - ref| / (1 + |ref|): the error measure the
     tolerances are stated in. NaN where either side is NaN counts as failure

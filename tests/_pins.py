@@ -309,6 +309,44 @@ def check_self_attention(orc, seed=26):
            "equal queries, all pairs == reduce")
 
 
+def check_bf16_round(orc, seed=27):
+    """Round-to-nearest-even to 8 significant bits: hand-checked ties and
+    neighbours, and torch's own float32 -> bfloat16 conversion on random
+    float32 values."""
+    import torch
+    one = 1.0
+    cases = {one + 2 ** -8: one, one + 3 * 2 ** -8: one + 2 ** -6, one + 2 ** -9: one,
+             one + 2 ** -8 + 2 ** -20: one + 2 ** -7, -(one + 2 ** -7 + 2 ** -8): -(one + 2 ** -6),
+             0.0: 0.0, 3.0: 3.0, 2 ** -100 * 1.00390625: 2 ** -100}
+    for a, want in cases.items():
+        assert orc.bf16_round(a) == want, (a, orc.bf16_round(a), want)
+    r = (_rng(seed).standard_normal(10000) * 10.0).astype(np.float32)
+    ref = torch.from_numpy(r).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(orc.bf16_round(r), ref)
+
+
+def check_layer(orc, seed=28):
+    """The layer is the projection followed by the scan: per (b, h), brute
+    force over k = x W_K[:, h], v = x W_V[:, h] (written out here with its own
+    indexing), the output rounded to bf16 or not."""
+    rng = _rng(seed)
+    B, N, Dm, H, d = 2, 9, 5, 3, 4
+    x = rng.standard_normal((B, N, Dm)).astype(np.float32)
+    w = (rng.standard_normal((Dm, 2 * H * d)) / 2).astype(np.float32)
+    q = rng.standard_normal((H, d)).astype(np.float32)
+    scale = 0.5
+    o = orc.layer_forward(x, w, q, scale, out_bf16=False)
+    assert o.shape == (B, N, H, d)
+    for b in range(B):
+        for h in range(H):
+            kh = np.einsum("nm,mj->nj", x[b].astype(np.float64), w[:, h * d:(h + 1) * d])
+            vh = np.einsum("nm,mj->nj", x[b].astype(np.float64), w[:, (H + h) * d:(H + h + 1) * d])
+            ref = brute.brute_scan(q[h], kh.astype(np.float32), vh.astype(np.float32), scale)
+            _close(o[b, :, h], ref, 1e-12, "layer vs projection + brute scan")
+    ob = orc.layer_forward(x, w, q, scale, out_bf16=True)
+    assert np.array_equal(ob, orc.bf16_round(o))
+
+
 def check_segmented(orc, seed=21):
     """Each packed sequence is scanned on its own: == brute force per segment;
     empty and length-1 segments included."""
@@ -413,5 +451,5 @@ def check_backward_closed_forms(orc, seed=24):
 
 ALL = [check_golden, check_scan_vs_definition, check_stats, check_single_token,
        check_running_mean, check_two_tokens, check_dominating_key, check_shift_invariance,
-       check_convex_hull, check_bracketing, check_reduce, check_step, check_append, check_self_attention, check_segmented,
+       check_convex_hull, check_bracketing, check_reduce, check_step, check_append, check_self_attention, check_bf16_round, check_layer, check_segmented,
        check_backward, check_backward_finite_differences, check_backward_closed_forms]

@@ -162,3 +162,41 @@ class _AppendMutant:
 def test_append_mutant_is_caught(fn):
     with pytest.raises((AssertionError, ValueError)):
         _pins.check_append(_AppendMutant(fn))
+
+
+def _layer_kv_swapped(x, w_kv, q, scale, out_bf16=True):
+    H, d = np.shape(q)
+    w = np.asarray(w_kv)
+    return oracle.layer_forward(x, np.concatenate([w[:, H * d:], w[:, :H * d]], axis=1), q, scale,
+                                out_bf16)
+
+
+def _layer_heads_interleaved(x, w_kv, q, scale, out_bf16=True):
+    # reads columns as [d][2][H] instead of [2][H][d]
+    H, d = np.shape(q)
+    w = np.asarray(w_kv).reshape(-1, d, 2, H).transpose(0, 2, 3, 1).reshape(-1, 2 * H * d)
+    return oracle.layer_forward(x, w, q, scale, out_bf16)
+
+
+def _layer_round_to_zero(x, w_kv, q, scale, out_bf16=True):
+    o = oracle.layer_forward(x, w_kv, q, scale, out_bf16=False)
+    if not out_bf16:
+        return o
+    m, e = np.frexp(o)
+    return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
+
+
+class _LayerMutant:
+    def __init__(self, fn):
+        self.layer_forward = fn
+
+    def __getattr__(self, name):
+        return getattr(oracle, name)
+
+
+@pytest.mark.parametrize("fn", [_layer_kv_swapped, _layer_heads_interleaved, _layer_round_to_zero],
+                         ids=["layer: W_K and W_V swapped", "layer: head columns interleaved",
+                              "layer: output truncated instead of rounded"])
+def test_layer_mutant_is_caught(fn):
+    with pytest.raises(AssertionError):
+        _pins.check_layer(_LayerMutant(fn))
