@@ -12,6 +12,8 @@ already resident in HBM:
   append                   : aaren_state_init + 16 aaren_append calls of 16
                              tokens, the same 256 tokens per stream
   backward                 : one aaren_scan_backward call on the dense batch
+  layer                    : 4 stacked aaren_layer_forward calls (rocBLAS
+                             projections + scan; tokens = B*N through all)
   self_attn                : one aaren_self_attention call (causal, one query
                              per token; matrix cores: TFLOP/s against the bf16
                              peak)
@@ -61,6 +63,7 @@ KERNEL_SOURCES = {
     "step": ["step.hip", "device.h", "layout.h"],
     "append": ["step.hip", "device.h", "layout.h"],
     "self_attention": ["self_attention.hip", "self_attention.h", "device.h", "layout.h"],
+    "layer": ["layer.hip", "scan.hip", "lookback.h", "device.h", "layout.h"],
     "reduce": ["reduce.hip", "device.h", "layout.h"],
 }
 
@@ -372,6 +375,47 @@ def make(name: str, device):
                                             f"one head (N={N}, d={d})")
         b.cpu = cpu
 
+    elif w.kind == "layer":
+        B, N, Dm, H, d, L = z["B"], z["N"], z["Dm"], z["H"], z["d"], z["layers"]
+        x, ws_, qs = wl.layer_inputs(B, N, Dm, H, d, L, w.seed, device=device)
+        scale = wl.default_scale(d)
+        bufs = [torch.empty(B, N, H, d, dtype=torch.bfloat16, device=device) for _ in range(2)]
+        work = torch.zeros(aaren.aaren_layer_workspace_size(B, N, H, d), dtype=torch.uint8,
+                           device=device)
+
+        def step():
+            h = x
+            for layer in range(L):
+                h = aaren.aaren_layer_forward(h.reshape(B, N, -1), ws_[layer], qs[layer], scale,
+                                              out=bufs[layer % 2], workspace=work)
+        b.step = step
+        b.kind = "layer"
+        b.unit = "tokens/s"
+        b.bound = "mfma"
+        # projection flops per layer (2 per multiply-add) plus the scan's 4d per token-head
+        b.flops_per_launch = sum(2 * B * N * (Dm if l == 0 else H * d) * 2 * H * d + 4 * d * B * N * H
+                                 for l in range(L))
+        b.units = B * N
+        b.bytes_per_launch = 0
+        b.config = {"workload": f"{L} stacked Aaren layers {b.describe}", "B": B, "N": N,
+                    "Dm": Dm, "H": H, "d": d, "layers": L, "in_dtype": "bf16",
+                    "out_dtype": "bf16", "flops_per_step": b.flops_per_launch}
+        b.kernel = "rocBLAS projection GEMMs + scan_kernel (the whole stack)"
+
+        def cpu(budget_s):
+            import oracle
+            xh = x[:1].float().cpu().numpy()
+            wh, qh = ws_[0].float().cpu().numpy(), qs[0].cpu().numpy()
+            done, t0 = 0, time.perf_counter()
+            while True:
+                oracle.layer_forward(xh, wh, qh, scale)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return done * N / L / dt, f"{done} pass(es) of the first layer over one batch row of {N} tokens (rate per stack of {L})"
+        b.cpu = cpu
+
     else:  # reduce
         B, H, N, d = z["B"], z["H"], z["N"], z["d"]
         q, k, v = wl.reduce_inputs(B, H, N, d, w.seed, device=device)
@@ -418,7 +462,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
                     choices=["single", "dense", "long_bf16", "ragged", "stream", "append",
-                             "reduce", "backward", "self_attn", "copy"])
+                             "reduce", "backward", "self_attn", "layer", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle time budget for cpu_baseline (0 to skip)")
     args = ap.parse_args()

@@ -31,7 +31,8 @@ EXPORTS = (
     "aaren_scan_workspace_size", "aaren_scan", "aaren_scan_segmented_workspace_size",
     "aaren_scan_segmented", "aaren_state_init", "aaren_step", "aaren_reduce_workspace_size",
     "aaren_reduce", "aaren_scan_backward_workspace_size", "aaren_scan_backward", "aaren_append",
-    "aaren_self_attention_workspace_size", "aaren_self_attention",
+    "aaren_self_attention_workspace_size", "aaren_self_attention", "aaren_scan_strided",
+    "aaren_layer_workspace_size", "aaren_layer_forward",
 )
 
 
@@ -62,6 +63,9 @@ def _load():
         "aaren_step": (I, [P, P, P, P, P, P, P, I64, I64, I64, F, I, I, P]),
         "aaren_append": (I, [P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P]),
         "aaren_self_attention_workspace_size": (SZ, [I64, I64, I64, I64]),
+        "aaren_scan_strided": (I, [P, P, P, P, P, I64, I64, I64, I64, P, P, F, I, I, P, SZ, P]),
+        "aaren_layer_workspace_size": (SZ, [I64, I64, I64, I64]),
+        "aaren_layer_forward": (I, [P, P, P, P, I64, I64, I64, I64, I64, F, I, P, SZ, P]),
         "aaren_self_attention": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, I, P, SZ, P]),
         "aaren_reduce_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_reduce": (I, [P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
@@ -100,14 +104,16 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need_cuda(*ts):
+def _need_cuda(*ts, strided=()):
+    """The device of the given tensors; every tensor must be on one GPU and,
+    unless it is one of `strided`, contiguous."""
     dev = None
     for t in ts:
         if t is None:
             continue
         if not t.is_cuda:
             raise ValueError("libaaren tensors must be on a GPU")
-        if not t.is_contiguous():
+        if not t.is_contiguous() and not any(t is x for x in strided):
             raise ValueError("libaaren tensors must be contiguous")
         if dev is None:
             dev = t.device
@@ -317,6 +323,63 @@ def aaren_append(q, k, v, m, u, w, scale=None, out_dtype=None, o=None, emit=True
                             default_scale(d) if scale is None else float(scale),
                             _dtype_code(k.dtype), _dtype_code(out_dtype), _stream(dev)))
     return o if emit else None
+
+
+def aaren_scan_strided(q, k, v, scale=None, out_dtype=None, out=None, workspace=None, lse=None,
+                       return_lse=False):
+    """aaren_scan over k, v given as [B,H,N,d] views with any strides whose
+    last dimension is contiguous (e.g. token-major [B,N,H,d] memory permuted
+    to [B,H,N,d]); out has k's layout unless given."""
+    dev = _need_cuda(q, k, v, out, workspace, lse, strided=(k, v, out))
+    B, H, N, d = k.shape
+    if v.shape != k.shape or v.stride() != k.stride() or q.shape != (H, d):
+        raise ValueError("expected q [H,d] and k, v [B,H,N,d] views with equal strides")
+    if k.stride(3) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty_like(k, dtype=out_dtype)
+    if out.shape != k.shape or out.stride(3) != 1:
+        raise ValueError("out must be a [B,H,N,d] view with a contiguous last dimension")
+    if lse is None and return_lse:
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    kvs = (ctypes.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+    os_ = (ctypes.c_int64 * 3)(out.stride(0), out.stride(1), out.stride(2))
+    need = aaren_scan_workspace_size(B, H, N, d)
+    ws = workspace if workspace is not None else _workspace("scan", need, dev, True)
+    _check(lib.aaren_scan_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                  kvs, os_, default_scale(d) if scale is None else float(scale),
+                                  _dtype_code(k.dtype), _dtype_code(out.dtype), _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(),
+                                  _stream(dev)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def aaren_layer_workspace_size(B, N, H, d) -> int:
+    return int(lib.aaren_layer_workspace_size(B, N, H, d))
+
+
+def aaren_layer_forward(x, w_kv, q, scale=None, out_dtype=None, out=None, workspace=None):
+    """One Aaren layer: x [B,N,Dm] bf16, w_kv [Dm, 2*H*d] bf16 (W_K | W_V),
+    q [H,d] float32 -> o [B,N,H,d] (bf16 by default, so that layers stack)."""
+    dev = _need_cuda(x, w_kv, q, out, workspace)
+    B, N, Dm = x.shape
+    H, d = q.shape
+    if w_kv.shape != (Dm, 2 * H * d) or x.dtype != torch.bfloat16 or w_kv.dtype != torch.bfloat16:
+        raise ValueError("expected bf16 x [B,N,Dm] and w_kv [Dm, 2*H*d]")
+    if q.dtype != torch.float32:
+        raise ValueError("q must be float32 [H,d]")
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty(B, N, H, d, dtype=out_dtype, device=dev)
+    need = aaren_layer_workspace_size(B, N, H, d)
+    ws = workspace if workspace is not None else _workspace("layer", need, dev, True)
+    _check(lib.aaren_layer_forward(_ptr(x), _ptr(w_kv), _ptr(q), _ptr(out), B, N, Dm, H, d,
+                                   default_scale(d) if scale is None else float(scale),
+                                   _dtype_code(out.dtype), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(),
+                                   _stream(dev)))
+    return out
 
 
 def aaren_self_attention_workspace_size(B, H, N, d) -> int:

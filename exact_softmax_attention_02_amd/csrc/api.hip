@@ -152,6 +152,12 @@ aaren_status prepare_counters(void *workspace, size_t need, hipStream_t stream)
 
 }  // namespace
 
+// Error reporting for the layer entry point (layer.hip); not exported.
+extern "C" aaren_status aaren_layer_fail(aaren_status s, const char *msg)
+{
+    return fail(s, "%s", msg);
+}
+
 AAREN_API int aaren_version(void)
 {
     return 100;  // 0.1.0
@@ -201,10 +207,15 @@ AAREN_API size_t aaren_scan_workspace_size(int64_t B, int64_t H, int64_t N, int6
     return scan_workspace_bytes(B * H, tiles, 0, d);
 }
 
-AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, float *lse,
-                                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                                  aaren_dtype in_dtype, aaren_dtype out_dtype, void *workspace,
-                                  size_t workspace_bytes, void *hip_stream)
+namespace {
+
+// The dense scan with explicit element strides {batch, head, row} for k/v and
+// for o (lse is always [B,H,N]).
+aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, const int64_t kvs[3],
+                        const int64_t os[3], float scale, aaren_dtype in_dtype,
+                        aaren_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                        void *hip_stream)
 {
     if (B < 0 || H < 0 || N < 0)
         return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
@@ -215,6 +226,13 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
         return fail(AAREN_ERR_UNSUPPORTED, "B*H*N*d overflows");
     if (elems == 0)
         return AAREN_OK;
+    const int64_t in_bytes = in_dtype == AAREN_F32 ? 4 : 2, out_bytes = out_dtype == AAREN_F32 ? 4 : 2;
+    for (int i = 0; i < 3; ++i) {
+        if (kvs[i] < 0 || os[i] < 0)
+            return fail(AAREN_ERR_INVALID_ARG, "negative stride");
+        if ((kvs[i] * in_bytes) % 16 || (os[i] * out_bytes) % 16)
+            return fail(AAREN_ERR_ALIGNMENT, "a stride is not a multiple of 16 bytes");
+    }
     CHECK(check_ptr(q, "q"));
     CHECK(check_ptr(k, "k"));
     CHECK(check_ptr(v, "v"));
@@ -248,8 +266,12 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
     p.rows = N;
     p.streams = B * H;
     p.H = H;
-    p.stream_stride = N * d;
-    p.row_stride = d;
+    p.batch_stride = kvs[0];
+    p.head_stride = kvs[1];
+    p.row_stride = kvs[2];
+    p.o_batch_stride = os[0];
+    p.o_head_stride = os[1];
+    p.o_row_stride = os[2];
     p.chunks = chunks;
     p.group = kGroupDense;
     p.chunks_padded = (uint32_t)chunks_padded;
@@ -267,6 +289,31 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
     CHECK(prepare_counters(workspace, counter_bytes(B * H), st));
     return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, false, st),
                       "scan launch");
+}
+
+}  // namespace
+
+AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, float *lse,
+                                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                  aaren_dtype in_dtype, aaren_dtype out_dtype, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream)
+{
+    const int64_t s[3] = {H * N * d, N * d, d};
+    return scan_dense(q, k, v, o, lse, B, H, N, d, s, s, scale, in_dtype, out_dtype, workspace,
+                      workspace_bytes, hip_stream);
+}
+
+AAREN_API aaren_status aaren_scan_strided(const void *q, const void *k, const void *v, void *o,
+                                          float *lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                                          const int64_t *kv_strides, const int64_t *o_strides,
+                                          float scale, aaren_dtype in_dtype,
+                                          aaren_dtype out_dtype, void *workspace,
+                                          size_t workspace_bytes, void *hip_stream)
+{
+    if (!kv_strides || !o_strides)
+        return fail(AAREN_ERR_INVALID_ARG, "strides are NULL");
+    return scan_dense(q, k, v, o, lse, B, H, N, d, kv_strides, o_strides, scale, in_dtype,
+                      out_dtype, workspace, workspace_bytes, hip_stream);
 }
 
 // ---- backward of the dense scan -----------------------------------------------
@@ -444,8 +491,9 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
     p.rows = total_tokens;
     p.streams = H;
     p.H = H;
-    p.stream_stride = d;
-    p.row_stride = H * d;
+    p.batch_stride = p.o_batch_stride = 0;  // one batch: the packed tokens
+    p.head_stride = p.o_head_stride = d;
+    p.row_stride = p.o_row_stride = H * d;
     p.chunks = chunks;
     p.group = kGroupPacked;
     p.chunks_padded = (uint32_t)chunks_padded;

@@ -70,8 +70,11 @@ struct ScanParams {
     int64_t rows;            // rows per stream: N (dense) or T (segmented)
     int64_t streams;         // B*H (dense) or H (segmented)
     int64_t H;
-    int64_t stream_stride;   // elements between stream bases: N*d or d
-    int64_t row_stride;      // elements between rows of a stream: d or H*d
+    // elements from the tensor start to row r of stream s = b*H + h:
+    //   b * batch_stride + h * head_stride + r * row_stride
+    // (k and v share one set, o has its own)
+    int64_t batch_stride, head_stride, row_stride;
+    int64_t o_batch_stride, o_head_stride, o_row_stride;
     int64_t chunks;          // tiles per stream
     uint32_t group;          // consecutive workgroups that serve one stream
     uint32_t chunks_padded;  // chunks rounded up to a multiple of group

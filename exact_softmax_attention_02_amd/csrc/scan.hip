@@ -101,7 +101,8 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     const int nvalid = left <= 0 ? 0 : (left >= R ? R : (int)left);
 
     // ---- issue every load of the group's rows first --------------------------
-    const int64_t base = stream * p.stream_stride + row0 * p.row_stride;  // column 0
+    const int64_t bat = stream / p.H, head = stream - bat * p.H;
+    const int64_t base = bat * p.batch_stride + head * p.head_stride + row0 * p.row_stride;  // column 0
     const Tin *kp = static_cast<const Tin *>(p.k) + base;
     const Tin *vp = static_cast<const Tin *>(p.v) + base;
     u32x4 kr[R], vr[R];
@@ -291,7 +292,8 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
         combine<E>(sh_cm, sh_cu, cw, pm, pu, pw, xm, xu, xw);
     }
 
-    Tout *op = static_cast<Tout *>(p.o) + base;
+    Tout *op = static_cast<Tout *>(p.o) + bat * p.o_batch_stride + head * p.o_head_stride +
+               row0 * p.o_row_stride;
     constexpr int LPL = (R + L - 1) / L;  // rows whose log-normaliser a lane stores
     float my_lse[LPL];
 #pragma unroll
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
                 ov[e] = xw[e] * inv;
             }
             xm = hi;
-            store_slice<D, Tin, Tout>(op + r * p.row_stride, gl, ov);
+            store_slice<D, Tin, Tout>(op + r * p.o_row_stride, gl, ov);
             if (p.lse && r % L == gl)  // L_k = (m + log2 u) ln 2, natural units
                 my_lse[r / L] = (xm + log2_fast(xu)) * kLn2;
         }

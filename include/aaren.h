@@ -131,6 +131,21 @@ aaren_status aaren_scan_backward(const void *q, const void *k, const void *v, co
                                  aaren_dtype in_dtype,
                                  void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* The same scan over tensors laid out with arbitrary element strides, e.g.
+ * token-major [B,N,H,d] as a projection produces them: row n of (b,h) of k
+ * and v starts at b*kv_strides[0] + h*kv_strides[1] + n*kv_strides[2]
+ * elements, and of o at the same with o_strides; the d elements of a row are
+ * contiguous. Every stride (in bytes) must be a multiple of 16 (ALIGNMENT
+ * otherwise, INVALID_ARG for a negative stride or NULL stride arrays). lse,
+ * if given, is [B,H,N] contiguous. Rows of o must not overlap rows of k or v.
+ * Workspace as for aaren_scan (same size query). */
+aaren_status aaren_scan_strided(const void *q, const void *k, const void *v, void *o,
+                                float *lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                                const int64_t *kv_strides /* host, [3] */,
+                                const int64_t *o_strides /* host, [3] */, float scale,
+                                aaren_dtype in_dtype, aaren_dtype out_dtype, void *workspace,
+                                size_t workspace_bytes, void *hip_stream);
+
 /* ---- many-to-many scan, packed variable-length batch -----------------------
  * The same output for a packed batch of independent sequences (each one is
  * scanned on its own; the pages do not treat packed batches, this is the
@@ -203,6 +218,29 @@ aaren_status aaren_reduce(const void *q, const void *k, const void *v, void *o,
                           int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                           aaren_dtype in_dtype, aaren_dtype out_dtype,
                           void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* ---- one Aaren layer ------------------------------------------------------
+ * "Attention as an RNN" (review, proposed method): an attention module
+ * whose query is a learned initial hidden state q (one per head) and whose
+ * many-to-many output is the prefix scan; layers are stacked like
+ * Transformer attention. Here (the pages print no layer formula; this is
+ * the plainest reading):
+ *   [K | V] = x [W_K | W_V]   (bf16 x, bf16 weights, fp32 products: rocBLAS)
+ *   o[b,n,h,:] = attention of q_h over K[b,0..n,h,:], V[b,0..n,h,:]
+ * x [B,N,Dm] bf16; w_kv [Dm, 2*H*d] bf16 row-major (columns 0..H*d-1 = W_K,
+ * the rest W_V, head h in columns h*d..h*d+d-1 of each); q [H,d] float32;
+ * o [B,N,H,d] (out_dtype; a stacked layer takes o, bf16, as its x with
+ * Dm = H*d). The workspace (aaren_layer_workspace_size) holds K|V in fp32
+ * and the scan's state; zero-fill it once before first use, as for
+ * aaren_scan. The first call on a device creates a rocBLAS handle (rocBLAS
+ * allocates its own workspace then); later calls allocate nothing.
+ * B*N*H = 0: OK, nothing done. Dm = 0 with rows: INVALID_ARG. Sizes beyond
+ * the 32-bit GEMM interface: UNSUPPORTED. A GEMM failure: HIP. */
+size_t aaren_layer_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d);
+aaren_status aaren_layer_forward(const void *x, const void *w_kv, const float *q, void *o,
+                                 int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t d,
+                                 float scale, aaren_dtype out_dtype, void *workspace,
+                                 size_t workspace_bytes, void *hip_stream);
 
 /* ---- self-attention, one query per token ------------------------------------
  * "Self-attention Does Not Need O(n^2) Memory", section 2: the single-query

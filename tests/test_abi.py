@@ -153,6 +153,36 @@ def test_self_attention_validation():
     assert aaren.aaren_self_attention_workspace_size(1, 1, 10, 100) == 0
 
 
+def test_scan_strided_validation():
+    st = (ctypes.c_int64 * 3)(8 * 100 * 64, 64, 8 * 64)
+    bad = (ctypes.c_int64 * 3)(8 * 100 * 64, 64, 8 * 64 + 2)     # 264 B rows: not 16-byte
+    neg = (ctypes.c_int64 * 3)(-1, 64, 512)
+    ss = lambda kv=st, o=st, **kw: L.aaren_scan_strided(A, A, A, A, None, 1, 8, 100, 64, kv, o,
+                                                        0.125, 0, 0, A, 1 << 24, None)
+    assert ss(kv=bad) == S["align"]
+    assert ss(o=bad) == S["align"]
+    assert ss(kv=neg) == S["arg"]
+    assert L.aaren_scan_strided(A, A, A, A, None, 1, 8, 100, 64, None, st, 0.125, 0, 0, A,
+                                1 << 24, None) == S["arg"]
+
+
+def test_layer_validation():
+    lf = lambda **kw: L.aaren_layer_forward(kw.get("x", A), A, A, A, 2, 10, kw.get("Dm", 32), 2,
+                                            kw.get("d", 64), 0.125, kw.get("out", 1),
+                                            kw.get("ws", A), kw.get("wsb", 1 << 24), None)
+    assert lf(d=32) == S["unsup"]
+    assert lf(out=5) == S["unsup"]
+    assert lf(Dm=0) == S["arg"]
+    assert lf(Dm=-1) == S["arg"]
+    assert lf(x=0) == S["arg"]
+    assert lf(x=A + 2) == S["align"]
+    assert lf(wsb=64) == S["ws"]
+    assert L.aaren_layer_forward(0, 0, 0, 0, 0, 10, 32, 2, 64, 0.125, 1, 0, 0, None) == 0
+    # [scan state][K|V in fp32]
+    assert aaren.aaren_layer_workspace_size(2, 100, 3, 64) == \
+        aaren.aaren_scan_workspace_size(2, 3, 100, 64) + 2 * 100 * 2 * 3 * 64 * 4
+
+
 def test_reduce_validation():
     rd = lambda **kw: L.aaren_reduce(A, A, A, A, kw.get("m", None), None, 1, 1, kw.get("N", 10),
                                      64, 0.125, 0, 0, kw.get("ws", A), kw.get("wsb", 1 << 20), None)

@@ -11,7 +11,7 @@ import torch
 import exact_softmax_attention_02_amd as aaren
 import oracle
 import workloads
-from _gpu import TOL, announce, check, dev, host32, scan_header_error
+from _gpu import TOL, TOL_BF16_OUT, announce, check, dev, host32, scan_header_error
 
 pytestmark = pytest.mark.gpu
 W = workloads.WORKLOADS
@@ -204,3 +204,26 @@ def test_self_attention_sampled_rows():
         worst = max(worst, check(o[:, :, a:b], ref, TOL[torch.bfloat16], f"rows {a}..{b}"))
         assert oracle.max_scaled_err(host32(lse[:, :, a:b]), rl) <= 1e-5
     print(f"self_attn: max scaled err over 384 rows x {B * H} heads {worst:.3e}")
+
+
+def test_layer_stack_in_full():
+    """The benchmark's four stacked layers at full size against the oracle's
+    stack (each layer's bf16 output feeds the next on both sides; the last
+    layer's GPU output, rounded once, against the unrounded oracle: bound as
+    for two layers, 2^-8 plus 1e-4 per layer)."""
+    w = W["layer"]
+    sz = w.sizes
+    B, N, Dm, H, d, L = sz["B"], sz["N"], sz["Dm"], sz["H"], sz["d"], sz["layers"]
+    announce(f"workload layer: {w.describe()}")
+    x, ws_, qs = workloads.layer_inputs(B, N, Dm, H, d, L, w.seed, device=dev())
+    scale = workloads.default_scale(d)
+    h = x
+    for layer in range(L):
+        h = aaren.aaren_layer_forward(h.reshape(B, N, -1), ws_[layer], qs[layer], scale)
+    torch.cuda.synchronize()
+    r = host32(x)
+    for layer in range(L):  # bf16 between layers, the last one unrounded
+        r = oracle.layer_forward(r.reshape(B, N, -1), host32(ws_[layer]), host32(qs[layer]), scale,
+                                 out_bf16=layer < L - 1)
+    err = check(h, r, TOL_BF16_OUT + L * 1e-4, "layer stack")
+    print(f"layer stack: max scaled err {err:.3e}")

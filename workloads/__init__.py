@@ -37,7 +37,7 @@ import torch
 class Workload:
     """One named workload: its kind, sizes, dtype and seed."""
     name: str
-    kind: str            # "dense" | "segmented" | "step" | "append" | "self_attention" | "reduce"
+    kind: str            # dense | segmented | step | append | self_attention | layer | reduce
     sizes: dict = field(default_factory=dict)
     dtype: str = "f32"   # input dtype: "f32" or "bf16"
     seed: int = 0
@@ -68,6 +68,8 @@ WORKLOADS = {
     # self-attention, one query per token, causal, at the pages' sequence length
     "self_attn": Workload("self_attn", "self_attention", dict(B=2, H=16, N=16384, d=128, causal=1),
                           "bf16", 7),
+    # stacked Aaren layers: bf16 projections (rocBLAS) + scan, Dm = H*d
+    "layer": Workload("layer", "layer", dict(B=8, N=4096, Dm=1024, H=16, d=64, layers=4), "bf16", 8),
     # one query over 2^20 keys
     "reduce": Workload("reduce", "reduce", dict(B=1, H=1, N=1 << 20, d=128), "f32", 6),
 }
@@ -153,6 +155,20 @@ def self_attention_inputs(B, H, N, d, seed, device="cpu", dtype="bf16"):
     v = torch.randn(B, H, N, d, generator=g, device=device, dtype=torch.float32)
     td = _torch_dtype(dtype)
     return q.to(td).contiguous(), k.to(td).contiguous(), v.to(td).contiguous()
+
+
+def layer_inputs(B, N, Dm, H, d, layers, seed, device="cpu"):
+    """x [B,N,Dm] bf16 N(0,1); per layer w_kv [Dm_l, 2*H*d] bf16 N(0, 1/Dm_l)
+    (Dm_l = Dm for the first layer, H*d after) and q [H,d] float32 N(0,1)."""
+    g = _gen(seed, device)
+    x = torch.randn(B, N, Dm, generator=g, device=device).to(torch.bfloat16)
+    ws, qs = [], []
+    for layer in range(layers):
+        dm = Dm if layer == 0 else H * d
+        ws.append((torch.randn(dm, 2 * H * d, generator=g, device=device) / dm ** 0.5)
+                  .to(torch.bfloat16))
+        qs.append(torch.randn(H, d, generator=g, device=device))
+    return x, ws, qs
 
 
 def reduce_inputs(B, H, N, d, seed, device="cpu", dtype="f32"):
