@@ -202,6 +202,22 @@ def self_attention(q, k, v, scale, causal: bool = True, rows=None, stats: bool =
     return (o, lse) if stats else o
 
 
+def mean_query_attention(hq, k, v, scale, stats: bool = False):
+    """Global-aggregation attention of the pooling network on the
+    efficient-transformer page (PoNet, "Global aggregation"): per (b,h) the
+    query g is the mean of hq over the N tokens (float64, then float32: every
+    query here is float32), and o is the attention of g over all N pairs
+    (the reduction). hq, k, v [B,H,N,d] -> o [B,H,d] (and g [B,H,d])."""
+    hq, k, v = _f32(hq), _f32(k), _f32(v)
+    B, H, N, d = k.shape
+    g = hq.astype(np.float64).mean(axis=2).astype(np.float32)
+    o = np.empty((B, H, d), np.float64)
+    for b in range(B):
+        for h in range(H):
+            o[b, h] = reduce(g[b, h][None], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], scale)[0, 0]
+    return (o, g) if stats else o
+
+
 def bf16_round(a):
     """Round float64 values to the nearest bfloat16 value (8 significant
     bits), ties to even; returned as float64. Normal range only."""

@@ -347,6 +347,30 @@ def check_layer(orc, seed=28):
     assert np.array_equal(ob, orc.bf16_round(o))
 
 
+def check_mean_query(orc, seed=29):
+    """Mean-query attention: torch's mean and softmax in float64 give the
+    same; equal query rows make it the plain reduction with that query; the
+    token order does not matter."""
+    import torch
+    rng = _rng(seed)
+    B, H, N, d = 2, 3, 41, 8
+    hq, k, v = (rng.standard_normal((B, H, N, d)).astype(np.float32) for _ in range(3))
+    scale = 0.6
+    o, g = orc.mean_query_attention(hq, k, v, scale, stats=True)
+    gt = torch.from_numpy(hq).double().mean(dim=2).float().double()
+    w = torch.softmax(scale * torch.einsum("bhnd,bhd->bhn", torch.from_numpy(k).double(), gt), dim=-1)
+    ref = torch.einsum("bhn,bhnd->bhd", w, torch.from_numpy(v).double()).numpy()
+    _close(o, ref, 1e-12, "mean query vs torch")
+    assert np.allclose(g, gt.float().numpy(), rtol=2.0 ** -23, atol=0)
+    qh = rng.standard_normal((H, d)).astype(np.float32)
+    same = np.ascontiguousarray(np.broadcast_to(qh[None, :, None, :], (B, H, N, d)))
+    _close(orc.mean_query_attention(same, k, v, scale), orc.reduce(qh, k, v, scale), 1e-13,
+           "equal query rows == reduce")
+    perm = rng.permutation(N)
+    _close(orc.mean_query_attention(hq[:, :, perm], k[:, :, perm], v[:, :, perm], scale), o,
+           1e-12, "token order")
+
+
 def check_segmented(orc, seed=21):
     """Each packed sequence is scanned on its own: == brute force per segment;
     empty and length-1 segments included."""
@@ -451,5 +475,5 @@ def check_backward_closed_forms(orc, seed=24):
 
 ALL = [check_golden, check_scan_vs_definition, check_stats, check_single_token,
        check_running_mean, check_two_tokens, check_dominating_key, check_shift_invariance,
-       check_convex_hull, check_bracketing, check_reduce, check_step, check_append, check_self_attention, check_bf16_round, check_layer, check_segmented,
+       check_convex_hull, check_bracketing, check_reduce, check_step, check_append, check_self_attention, check_bf16_round, check_layer, check_mean_query, check_segmented,
        check_backward, check_backward_finite_differences, check_backward_closed_forms]

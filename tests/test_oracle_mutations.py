@@ -200,3 +200,29 @@ class _LayerMutant:
 def test_layer_mutant_is_caught(fn):
     with pytest.raises(AssertionError):
         _pins.check_layer(_LayerMutant(fn))
+
+
+def _mean_query_summed(hq, k, v, scale, stats=False):
+    hq = np.asarray(hq, np.float32)
+    return oracle.mean_query_attention(hq * np.float32(hq.shape[2]), k, v, scale, stats)
+
+
+def _mean_query_first_token(hq, k, v, scale, stats=False):
+    hq = np.asarray(hq, np.float32)
+    return oracle.mean_query_attention(np.repeat(hq[:, :, :1], hq.shape[2], axis=2), k, v, scale,
+                                       stats)
+
+
+class _MeanQueryMutant:
+    def __init__(self, fn):
+        self.mean_query_attention = fn
+
+    def __getattr__(self, name):
+        return getattr(oracle, name)
+
+
+@pytest.mark.parametrize("fn", [_mean_query_summed, _mean_query_first_token],
+                         ids=["mean query: sum without 1/N", "mean query: first token only"])
+def test_mean_query_mutant_is_caught(fn):
+    with pytest.raises(AssertionError):
+        _pins.check_mean_query(_MeanQueryMutant(fn))
