@@ -12,6 +12,7 @@ already resident in HBM:
   append                   : aaren_state_init + 16 aaren_append calls of 16
                              tokens, the same 256 tokens per stream
   backward                 : one aaren_scan_backward call on the dense batch
+  mean_query               : one aaren_mean_query_attention call (keys/s)
   layer                    : 4 stacked aaren_layer_forward calls (rocBLAS
                              projections + scan; tokens = B*N through all)
   self_attn                : one aaren_self_attention call (causal, one query
@@ -65,6 +66,7 @@ KERNEL_SOURCES = {
     "self_attention": ["self_attention.hip", "self_attention.h", "device.h", "layout.h"],
     "layer": ["layer.hip", "scan.hip", "lookback.h", "device.h", "layout.h"],
     "reduce": ["reduce.hip", "device.h", "layout.h"],
+    "mean_query": ["reduce.hip", "device.h", "layout.h"],
 }
 
 
@@ -375,6 +377,43 @@ def make(name: str, device):
                                             f"one head (N={N}, d={d})")
         b.cpu = cpu
 
+    elif w.kind == "mean_query":
+        B, H, N, d = z["B"], z["H"], z["N"], z["d"]
+        hq, k, v = wl.mean_query_inputs(B, H, N, d, w.seed, device=device)
+        scale = wl.default_scale(d)
+        o = torch.empty(B, H, d, device=device)
+        ws = torch.empty(aaren.aaren_mean_query_attention_workspace_size(B, H, N, d),
+                         dtype=torch.uint8, device=device)
+        b.bytes_per_launch = 3 * k.numel() * 4 + o.numel() * 4
+        b.sets = n_sets(b.bytes_per_launch)
+        bufs = [(hq, k, v)] + [(hq.clone(), k.clone(), v.clone()) for _ in range(b.sets - 1)]
+        turn = [0]
+
+        def step():
+            hh, kk, vv = bufs[turn[0] % b.sets]
+            turn[0] += 1
+            aaren.aaren_mean_query_attention(hh, kk, vv, scale, out=o, workspace=ws)
+        b.step = step
+        b.kind = "mean_query"
+        b.unit = "keys/s"
+        b.units = B * H * N
+        b.config = {"workload": f"mean-query attention {b.describe}", "B": B, "H": H, "N": N,
+                    "d": d, "in_dtype": "f32", "out_dtype": "f32"}
+        b.kernel = "mean_partial_kernel + mean_final_kernel + reduce kernels"
+
+        def cpu(budget_s):
+            import oracle
+            hh, kh, vh = (t[:1, :1].cpu().numpy() for t in (hq, k, v))
+            done, t0 = 0, time.perf_counter()
+            while True:
+                oracle.mean_query_attention(hh, kh, vh, scale)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return done * N / dt, f"{done} pass(es) over one (b,h) of {N} pairs (one unit: 1 thread)"
+        b.cpu = cpu
+
     elif w.kind == "layer":
         B, N, Dm, H, d, L = z["B"], z["N"], z["Dm"], z["H"], z["d"], z["layers"]
         x, ws_, qs = wl.layer_inputs(B, N, Dm, H, d, L, w.seed, device=device)
@@ -462,7 +501,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
                     choices=["single", "dense", "long_bf16", "ragged", "stream", "append",
-                             "reduce", "backward", "self_attn", "layer", "copy"])
+                             "reduce", "backward", "self_attn", "layer", "mean_query", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle time budget for cpu_baseline (0 to skip)")
     args = ap.parse_args()
@@ -506,7 +545,7 @@ def main():
     if args.cpu_seconds > 0 and b.cpu is not None:
         import oracle
         rate, sample = b.cpu(args.cpu_seconds)
-        cores = oracle.threads() if args.workload != "reduce" else 1
+        cores = oracle.threads() if args.workload not in ("reduce", "mean_query") else 1
         cpu = {"value": rate, "unit": b.unit, "cores": cores, "kind": "oracle", "sample": sample}
 
     line = {

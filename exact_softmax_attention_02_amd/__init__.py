@@ -33,6 +33,7 @@ EXPORTS = (
     "aaren_reduce", "aaren_scan_backward_workspace_size", "aaren_scan_backward", "aaren_append",
     "aaren_self_attention_workspace_size", "aaren_self_attention", "aaren_scan_strided",
     "aaren_layer_workspace_size", "aaren_layer_forward",
+    "aaren_mean_query_attention_workspace_size", "aaren_mean_query_attention",
 )
 
 
@@ -65,6 +66,8 @@ def _load():
         "aaren_self_attention_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_scan_strided": (I, [P, P, P, P, P, I64, I64, I64, I64, P, P, F, I, I, P, SZ, P]),
         "aaren_layer_workspace_size": (SZ, [I64, I64, I64, I64]),
+        "aaren_mean_query_attention_workspace_size": (SZ, [I64, I64, I64, I64]),
+        "aaren_mean_query_attention": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
         "aaren_layer_forward": (I, [P, P, P, P, I64, I64, I64, I64, I64, F, I, P, SZ, P]),
         "aaren_self_attention": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, I, P, SZ, P]),
         "aaren_reduce_workspace_size": (SZ, [I64, I64, I64, I64]),
@@ -380,6 +383,33 @@ def aaren_layer_forward(x, w_kv, q, scale=None, out_dtype=None, out=None, worksp
                                    0 if ws is None else ws.numel() * ws.element_size(),
                                    _stream(dev)))
     return out
+
+
+def aaren_mean_query_attention_workspace_size(B, H, N, d) -> int:
+    return int(lib.aaren_mean_query_attention_workspace_size(B, H, N, d))
+
+
+def aaren_mean_query_attention(hq, k, v, scale=None, out_dtype=None, out=None, g_out=None,
+                               return_query=False, workspace=None):
+    """Attention of each (b,h)'s mean query over all its pairs: hq, k, v
+    [B,H,N,d] -> o [B,H,d] (and the mean queries g [B,H,d] float32)."""
+    dev = _need_cuda(hq, k, v, out, g_out, workspace)
+    B, H, N, d = k.shape
+    if hq.shape != k.shape or v.shape != k.shape or not (hq.dtype == k.dtype == v.dtype):
+        raise ValueError("expected hq, k, v [B,H,N,d] of one dtype")
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty(B, H, d, dtype=out_dtype, device=dev)
+    if g_out is None and return_query:
+        g_out = torch.empty(B, H, d, dtype=torch.float32, device=dev)
+    need = aaren_mean_query_attention_workspace_size(B, H, N, d)
+    ws = workspace if workspace is not None else _workspace("meanq", need, dev, False)
+    _check(lib.aaren_mean_query_attention(_ptr(hq), _ptr(k), _ptr(v), _ptr(out), _ptr(g_out), B, H,
+                                          N, d, default_scale(d) if scale is None else float(scale),
+                                          _dtype_code(k.dtype), _dtype_code(out.dtype), _ptr(ws),
+                                          0 if ws is None else ws.numel() * ws.element_size(),
+                                          _stream(dev)))
+    return (out, g_out) if (return_query or g_out is not None) else out
 
 
 def aaren_self_attention_workspace_size(B, H, N, d) -> int:

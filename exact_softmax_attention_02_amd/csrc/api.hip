@@ -728,6 +728,86 @@ AAREN_API size_t aaren_reduce_workspace_size(int64_t B, int64_t H, int64_t N, in
     return n < 0 ? 0 : (size_t)n;
 }
 
+namespace {
+
+size_t mean_query_parts_bytes(int64_t units, int64_t parts, int64_t d, size_t *reduce_b,
+                              size_t *mean_b)
+{
+    *reduce_b = aaren::round256((size_t)units * parts * aaren::slot_words((int)d) * 4);
+    *mean_b = aaren::round256((size_t)units * parts * d * 8);
+    return *reduce_b + *mean_b + aaren::round256((size_t)units * d * 4);
+}
+
+}  // namespace
+
+AAREN_API size_t aaren_mean_query_attention_workspace_size(int64_t B, int64_t H, int64_t N,
+                                                           int64_t d)
+{
+    if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128))
+        return 0;
+    const int64_t units = mul_checked({B, H});
+    if (units < 0 || mul_checked({B, H, N, d}) < 0)
+        return 0;
+    size_t rb, mb;
+    return mean_query_parts_bytes(units, reduce_parts(units, N, d), d, &rb, &mb);
+}
+
+AAREN_API aaren_status aaren_mean_query_attention(const void *hq, const void *k, const void *v,
+                                                  void *o, float *g_out, int64_t B, int64_t H,
+                                                  int64_t N, int64_t d, float scale,
+                                                  aaren_dtype in_dtype, aaren_dtype out_dtype,
+                                                  void *workspace, size_t workspace_bytes,
+                                                  void *hip_stream)
+{
+    if (B < 0 || H < 0 || N < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
+                    (long long)B, (long long)H, (long long)N);
+    CHECK(check_common(d, in_dtype, out_dtype));
+    const int64_t units = mul_checked({B, H});
+    if (units < 0 || mul_checked({B, H, N, d}) < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "B*H*N*d overflows");
+    if (units == 0)
+        return AAREN_OK;
+    if (N == 0)
+        return fail(AAREN_ERR_INVALID_ARG, "N = 0: the mean of no queries has no value");
+    if (units > 0x7fffffff / aaren::kReduceMaxParts)
+        return fail(AAREN_ERR_UNSUPPORTED, "B*H = %lld is too large", (long long)units);
+    CHECK(check_ptr(hq, "hq"));
+    CHECK(check_ptr(k, "k"));
+    CHECK(check_ptr(v, "v"));
+    CHECK(check_ptr(o, "o"));
+    if (g_out)
+        CHECK(check_ptr(g_out, "g_out"));
+    const int64_t parts = reduce_parts(units, N, d);
+    size_t rb, mb;
+    const size_t need = mean_query_parts_bytes(units, parts, d, &rb, &mb);
+    if (!workspace || workspace_bytes < need)
+        return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    need);
+    if (!aligned16(workspace))
+        return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    aaren::ReduceParams p{};
+    p.q = hq;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.partials = reinterpret_cast<float *>(ws);
+    p.mean_partials = reinterpret_cast<double *>(ws + rb);
+    p.q_mean = reinterpret_cast<float *>(ws + rb + mb);
+    p.g_out = g_out;
+    p.q_unit = p.q_mean;
+    p.units = units;
+    p.H = H;
+    p.N = N;
+    p.parts = parts;
+    p.rows_per_part = ceil_div(N, parts);
+    p.qscale = scale * 1.44269504088896340736f;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    CHECK(hip_status(aaren::launch_mean_query(p, (int)d, in_dtype, st), "mean-query launch"));
+    return hip_status(aaren::launch_reduce(p, (int)d, in_dtype, out_dtype, st), "reduce launch");
+}
+
 AAREN_API aaren_status aaren_reduce(const void *q, const void *k, const void *v, void *o,
                                     float *m_out, float *u_out, int64_t B, int64_t H, int64_t N,
                                     int64_t d, float scale, aaren_dtype in_dtype,

@@ -108,6 +108,10 @@ struct ReduceParams {
     float *m_out;
     float *u_out;
     float *partials;      // [units][parts][slot_words(d)] floats: m, u, w[d]
+    const float *q_unit;  // per-unit float32 queries [units][d], or null: q [H][d] in the input dtype
+    double *mean_partials;  // mean-query pass: [units][parts][d] column sums
+    float *q_mean;        // mean-query pass output: [units][d]
+    float *g_out;         // optional copy of q_mean for the caller
     int64_t units;        // B*H
     int64_t H;
     int64_t N;
@@ -117,6 +121,7 @@ struct ReduceParams {
 };
 
 constexpr int kReduceMaxParts = 512;
+hipError_t launch_mean_query(const ReduceParams &p, int D, aaren_dtype in, hipStream_t stream);
 
 // Rows one backward tile covers: 128 (16 lane groups of 8 rows for d = 64,
 // 16 groups over 8 waves for d = 128); five row tensors are held per lane.

@@ -46,7 +46,11 @@ __global__ __launch_bounds__(64 * WAVES) void reduce_partial_kernel(const Reduce
 
     using SL = Slice<D, Tin>;
     float qv[E];
-    widen<Tin>(load_slice<D, Tin, false>(static_cast<const Tin *>(p.q) + (unit % p.H) * D, gl), qv);
+    if (p.q_unit)  // one float32 query per (b,h), at this lane's slice columns
+        load_state<D, Tin>(p.q_unit + unit * D, gl, qv);
+    else
+        widen<Tin>(load_slice<D, Tin, false>(static_cast<const Tin *>(p.q) + (unit % p.H) * D, gl),
+                   qv);
 #pragma unroll
     for (int e = 0; e < E; ++e)
         qv[e] *= p.qscale;
@@ -217,6 +221,84 @@ __global__ __launch_bounds__(kFinalThreads) void reduce_final_kernel(const Reduc
         if (p.u_out)
             p.u_out[unit] = U;
     }
+}
+
+// Mean query of each (b,h) (the global-aggregation query of the pooling
+// network reviewed on the efficient-transformer page: the average of the
+// query projections): g = (1/N) sum_n hq[n]. Column sums in float64, each
+// workgroup over one chunk of rows (the reduction's chunks), then the chunks
+// added in order, so g is the same bits on every run; g is rounded to float32
+// once, the precision of every query in this library.
+template <int D, typename Tin>
+__global__ __launch_bounds__(256) void mean_partial_kernel(const ReduceParams p)
+{
+    using G = RowGeo<D, Tin>;
+    using SL = Slice<D, Tin>;
+    constexpr int E = G::kElems, L = G::kLanes, NG = 4 * G::kGroupsPerWave;
+    __shared__ double sh[NG][D];
+    const int tid = threadIdx.x, gl = tid % L, grp = tid / L;
+    const int64_t unit = blockIdx.x / p.parts, part = blockIdx.x - unit * p.parts;
+    const int64_t begin = part * p.rows_per_part;
+    int64_t end = begin + p.rows_per_part;
+    end = end < p.N ? end : p.N;
+    const Tin *hb = static_cast<const Tin *>(p.q) + unit * p.N * D;
+    double acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        acc[e] = 0.0;
+    for (int64_t row = begin + grp; row < end; row += NG) {
+        float x[E];
+        widen<Tin>(load_slice<D, Tin, true>(hb + row * D, gl), x);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            acc[e] += (double)x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        sh[grp][SL::col(gl, e)] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        double t = 0.0;
+        for (int g = 0; g < NG; ++g)
+            t += sh[g][tid];
+        p.mean_partials[(size_t)blockIdx.x * D + tid] = t;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void mean_final_kernel(const ReduceParams p)
+{
+    const int col = threadIdx.x;
+    const int64_t unit = blockIdx.x;
+    const double *base = p.mean_partials + (size_t)unit * p.parts * D;
+    double t = 0.0;
+    for (int64_t i = 0; i < p.parts; ++i)
+        t += base[(size_t)i * D + col];
+    const float g = (float)(t / (double)p.N);
+    p.q_mean[unit * D + col] = g;
+    if (p.g_out)
+        p.g_out[unit * D + col] = g;
+}
+
+template <int D>
+static hipError_t mean_one(const ReduceParams &p, aaren_dtype in, hipStream_t stream)
+{
+    if (in == AAREN_F32)
+        hipLaunchKernelGGL((mean_partial_kernel<D, float>), dim3((unsigned)(p.units * p.parts)),
+                           dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((mean_partial_kernel<D, bf16>), dim3((unsigned)(p.units * p.parts)),
+                           dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((mean_final_kernel<D>), dim3((unsigned)p.units), dim3(D), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_mean_query(const ReduceParams &p, int D, aaren_dtype in, hipStream_t stream)
+{
+    return D == 64 ? mean_one<64>(p, in, stream) : mean_one<128>(p, in, stream);
 }
 
 template <int D, typename Tin>

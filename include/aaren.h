@@ -264,6 +264,25 @@ aaren_status aaren_self_attention(const void *q, const void *k, const void *v, v
                                   aaren_dtype out_dtype, void *workspace,
                                   size_t workspace_bytes, void *hip_stream);
 
+/* ---- mean-query attention ---------------------------------------------------
+ * The global aggregation of the pooling network reviewed on the
+ * efficient-transformer page (PoNet, "Global aggregation" and its two
+ * equations): the query of each sequence is the average of its query
+ * projections, g = (1/N) sum_n hq_n, and attends over all N keys and values
+ * (the page's value argument is printed as H_Q; read as H_V). It is the
+ * many-to-one reduction above with one query per (b,h):
+ *   hq, k, v [B,H,N,d] (in_dtype);  o [B,H,d] (out_dtype);
+ *   g_out [B,H,d] float32 or NULL: the mean queries used.
+ * g is summed in float64 in a fixed order and rounded to float32 once.
+ * N = 0 with B*H > 0: INVALID_ARG; B*H = 0: OK, nothing done. Workspace from
+ * the size query; no zero-fill needed. Other statuses as for aaren_reduce. */
+size_t aaren_mean_query_attention_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d);
+aaren_status aaren_mean_query_attention(const void *hq, const void *k, const void *v, void *o,
+                                        float *g_out, int64_t B, int64_t H, int64_t N,
+                                        int64_t d, float scale, aaren_dtype in_dtype,
+                                        aaren_dtype out_dtype, void *workspace,
+                                        size_t workspace_bytes, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -183,6 +183,19 @@ def test_layer_validation():
         aaren.aaren_scan_workspace_size(2, 3, 100, 64) + 2 * 100 * 2 * 3 * 64 * 4
 
 
+def test_mean_query_validation():
+    mq = lambda **kw: L.aaren_mean_query_attention(A, A, A, kw.get("o", A), kw.get("g", None), 1, 2,
+                                                   kw.get("N", 100), 64, 0.125, 0, 0,
+                                                   kw.get("ws", A), kw.get("wsb", 1 << 24), None)
+    assert mq(N=0) == S["arg"]
+    assert mq(o=0) == S["arg"]
+    assert mq(g=A + 4) == S["align"]
+    assert mq(wsb=16) == S["ws"]
+    assert L.aaren_mean_query_attention(0, 0, 0, 0, None, 0, 2, 5, 64, 0.125, 0, 0, 0, 0,
+                                        None) == 0
+    assert aaren.aaren_mean_query_attention_workspace_size(1, 2, 100, 96) == 0
+
+
 def test_reduce_validation():
     rd = lambda **kw: L.aaren_reduce(A, A, A, A, kw.get("m", None), None, 1, 1, kw.get("N", 10),
                                      64, 0.125, 0, 0, kw.get("ws", A), kw.get("wsb", 1 << 20), None)

@@ -70,6 +70,8 @@ WORKLOADS = {
                           "bf16", 7),
     # stacked Aaren layers: bf16 projections (rocBLAS) + scan, Dm = H*d
     "layer": Workload("layer", "layer", dict(B=8, N=4096, Dm=1024, H=16, d=64, layers=4), "bf16", 8),
+    # global-aggregation attention: each (b,h)'s mean query over its 65536 pairs
+    "mean_query": Workload("mean_query", "mean_query", dict(B=4, H=8, N=65536, d=128), "f32", 9),
     # one query over 2^20 keys
     "reduce": Workload("reduce", "reduce", dict(B=1, H=1, N=1 << 20, d=128), "f32", 6),
 }
@@ -169,6 +171,17 @@ def layer_inputs(B, N, Dm, H, d, layers, seed, device="cpu"):
                   .to(torch.bfloat16))
         qs.append(torch.randn(H, d, generator=g, device=device))
     return x, ws, qs
+
+
+def mean_query_inputs(B, H, N, d, seed, device="cpu", dtype="f32"):
+    """hq, K, V [B,H,N,d]: hq N(0.5, 1) (so the mean query is of order 0.5
+    and the weights are not all equal), K and V N(0,1)."""
+    g = _gen(seed, device)
+    hq = torch.randn(B, H, N, d, generator=g, device=device, dtype=torch.float32) + 0.5
+    k = torch.randn(B, H, N, d, generator=g, device=device, dtype=torch.float32)
+    v = torch.randn(B, H, N, d, generator=g, device=device, dtype=torch.float32)
+    td = _torch_dtype(dtype)
+    return hq.to(td).contiguous(), k.to(td).contiguous(), v.to(td).contiguous()
 
 
 def reduce_inputs(B, H, N, d, seed, device="cpu", dtype="f32"):
