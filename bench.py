@@ -440,6 +440,7 @@ def make(name: str, device):
                     "Dm": Dm, "H": H, "d": d, "layers": L, "in_dtype": "bf16",
                     "out_dtype": "bf16", "flops_per_step": b.flops_per_launch}
         b.kernel = "rocBLAS projection GEMMs + scan_kernel (the whole stack)"
+        b.dispatches_per_launch = L  # one GEMM and one scan per layer
 
         def cpu(budget_s):
             import oracle
@@ -531,6 +532,8 @@ def main():
     launch_s = ms / 1e3 / b.launches_per_step
     achieved = b.bytes_per_launch / launch_s / 1e9
     traffic = measured_traffic(b.kind, args.workload) if b.kind != "copy" else None
+    if traffic is not None:
+        traffic *= getattr(b, "dispatches_per_launch", 1)  # counters are per kernel dispatch
     if getattr(b, "bound", "hbm") == "mfma":
         tflops = b.flops_per_launch / launch_s / 1e12
         roofline = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
