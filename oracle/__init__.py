@@ -141,6 +141,29 @@ def step(q, k_t, v_t, state, scale):
     return o
 
 
+def scan_segmented_backward(q, k, v, dout, offsets, scale):
+    """Gradients of the packed many-to-many output: q [H,d]; k, v, dout [T,H,d];
+    offsets [S+1]. Each sequence is scanned on its own, so its gradients are
+    the dense gradients of that sequence (scan_backward), and dq adds every
+    sequence's dq. Returns dq [H,d], dk, dv [T,H,d] float64."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    offsets = np.asarray(offsets, np.int64)
+    T, H, d = k.shape
+    dq = np.zeros((H, d), np.float64)
+    dk = np.zeros((T, H, d), np.float64)
+    dv = np.zeros((T, H, d), np.float64)
+    for s in range(offsets.size - 1):
+        a, b = int(offsets[s]), int(offsets[s + 1])
+        if a == b:
+            continue
+        per = [np.ascontiguousarray(x[a:b].transpose(1, 0, 2)[None]) for x in (k, v, dout)]
+        rq, rk, rv = scan_backward(q, per[0], per[1], per[2], scale)
+        dq += rq
+        dk[a:b] = rk[0].transpose(1, 0, 2)
+        dv[a:b] = rv[0].transpose(1, 0, 2)
+    return dq, dk, dv
+
+
 def append(q, k, v, state, scale):
     """Append T tokens to every (stream, head) state: k, v [T,S,H,d]
     (time-major, k[t] is one step's keys), state = (m, u, w) float64 updated

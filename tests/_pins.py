@@ -424,6 +424,32 @@ def check_backward(orc, seed=22):
             _close(dq[h], acc, 1e-11, "dq (batch sum) vs definition")
 
 
+def check_segmented_backward(orc, seed=30):
+    """Packed gradients == torch autograd through a packed forward written
+    out here (a softmax over each sequence's prefix, sequence by sequence),
+    with empty, length-1 and longer sequences; dq adds all sequences."""
+    import torch
+    rng = _rng(seed)
+    lengths = np.array([3, 0, 1, 17, 0, 9, 1], np.int64)
+    offs = np.concatenate([[0], np.cumsum(lengths)])
+    T, H, d, scale = int(offs[-1]), 2, 5, 0.7
+    q = rng.standard_normal((H, d)).astype(np.float32)
+    k = (2 * rng.standard_normal((T, H, d))).astype(np.float32)
+    v, g = (rng.standard_normal((T, H, d)).astype(np.float32) for _ in range(2))
+    dq, dk, dv = orc.scan_segmented_backward(q, k, v, g, offs, scale)
+    qt, kt, vt = (torch.tensor(x.astype(np.float64), requires_grad=True) for x in (q, k, v))
+    rows = []
+    for t in range(T):
+        a = int(offs[np.searchsorted(offs, t, side="right") - 1])
+        s_ = scale * (kt[a:t + 1] * qt[None]).sum(-1)          # [len, H]
+        w = torch.softmax(s_, dim=0)
+        rows.append((w[..., None] * vt[a:t + 1]).sum(0))       # [H, d]
+    torch.stack(rows).backward(torch.tensor(g.astype(np.float64)))
+    _close(dk, kt.grad.numpy(), 1e-11, "packed dk vs autograd")
+    _close(dv, vt.grad.numpy(), 1e-11, "packed dv vs autograd")
+    _close(dq, qt.grad.numpy(), 1e-11, "packed dq vs autograd")
+
+
 def check_backward_finite_differences(orc, seed=23):
     """Central differences of loss = sum(g * o) through the forward oracle."""
     rng = _rng(seed)
@@ -476,4 +502,4 @@ def check_backward_closed_forms(orc, seed=24):
 ALL = [check_golden, check_scan_vs_definition, check_stats, check_single_token,
        check_running_mean, check_two_tokens, check_dominating_key, check_shift_invariance,
        check_convex_hull, check_bracketing, check_reduce, check_step, check_append, check_self_attention, check_bf16_round, check_layer, check_mean_query, check_segmented,
-       check_backward, check_backward_finite_differences, check_backward_closed_forms]
+       check_backward, check_segmented_backward, check_backward_finite_differences, check_backward_closed_forms]

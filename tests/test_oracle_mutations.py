@@ -226,3 +226,35 @@ class _MeanQueryMutant:
 def test_mean_query_mutant_is_caught(fn):
     with pytest.raises(AssertionError):
         _pins.check_mean_query(_MeanQueryMutant(fn))
+
+
+def _seg_bwd_unseparated(q, k, v, dout, offsets, scale):
+    T = np.shape(k)[0]
+    return oracle.scan_segmented_backward(q, k, v, dout, np.array([0, T]), scale)
+
+
+def _seg_bwd_last_dq(q, k, v, dout, offsets, scale):
+    dq, dk, dv = oracle.scan_segmented_backward(q, k, v, dout, offsets, scale)
+    return _only_last_dq(q, k, v, dout, np.asarray(offsets), scale), dk, dv
+
+
+def _only_last_dq(q, k, v, dout, o, scale):
+    a, b = int(o[-2]), int(o[-1])
+    sub = [np.ascontiguousarray(np.asarray(x)[a:b].transpose(1, 0, 2)[None]) for x in (k, v, dout)]
+    return oracle.scan_backward(q, sub[0], sub[1], sub[2], scale)[0]
+
+
+class _SegBwdMutant:
+    def __init__(self, fn):
+        self.scan_segmented_backward = fn
+
+    def __getattr__(self, name):
+        return getattr(oracle, name)
+
+
+@pytest.mark.parametrize("fn", [_seg_bwd_unseparated, _seg_bwd_last_dq],
+                         ids=["packed backward: sequences not separated",
+                              "packed backward: dq of the last sequence only"])
+def test_segmented_backward_mutant_is_caught(fn):
+    with pytest.raises(AssertionError):
+        _pins.check_segmented_backward(_SegBwdMutant(fn))
