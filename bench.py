@@ -12,6 +12,8 @@ already resident in HBM:
   append                   : aaren_state_init + 16 aaren_append calls of 16
                              tokens, the same 256 tokens per stream
   backward                 : one aaren_scan_backward call on the dense batch
+  ragged_backward          : one aaren_scan_segmented_backward call on a packed
+                             batch of 1024 sequences
   mean_query               : one aaren_mean_query_attention call (keys/s)
   layer                    : 4 stacked aaren_layer_forward calls (rocBLAS
                              projections + scan; tokens = B*N through all)
@@ -182,6 +184,48 @@ def make(name: str, device):
                     break
             dt = time.perf_counter() - t0
             return done * B * H * N / dt, f"{done} pass(es) over {B}x{H}x{N} (d={d}) gradients"
+        b.cpu = cpu
+        return b
+
+    if name == "ragged_backward":
+        H, d = z["H"], z["d"]
+        lengths = wl.segment_lengths(z["num_seqs"], z["max_len"], w.seed)
+        q, k, v, offs = wl.segmented_inputs(lengths, H, d, w.seed, device=device)
+        T = int(lengths.sum())
+        scale = wl.default_scale(d)
+        o, lse = aaren.aaren_scan_segmented(q, k, v, offs, scale, return_lse=True)
+        g = torch.randn(T, H, d, device=device,
+                        generator=torch.Generator(device=device).manual_seed(w.seed + 100))
+        dq, dk, dv = torch.empty(H, d, device=device), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.zeros(aaren.aaren_scan_segmented_backward_workspace_size(len(lengths), T, H, d),
+                         dtype=torch.uint8, device=device)
+        b.step = lambda: aaren.aaren_scan_segmented_backward(q, k, v, o, g, lse, offs, scale, dq=dq,
+                                                             dk=dk, dv=dv, workspace=ws)
+        b.kind = "backward"
+        b.units = H * T
+        b.bytes_per_launch = 6 * T * H * d * 4 + T * H * 4 + offs.numel() * 8 + H * d * 4
+        b.config = {"workload": f"gradients of the packed many-to-many scan {b.describe}",
+                    "num_seqs": len(lengths), "total_tokens": T, "H": H, "d": d,
+                    "in_dtype": "f32", "out_dtype": "f32"}
+        b.kernel = "scan_backward_kernel (packed) + scan_backward_dq_kernel"
+
+        def cpu(budget_s):
+            import oracle
+            ho = offs.cpu().numpy()
+            n = 1
+            while n < len(lengths) and ho[n] < 500_000:
+                n += 1
+            qh = q.cpu().numpy()
+            kh, vh, gh = (t[:ho[n]].cpu().numpy() for t in (k, v, g))
+            done, t0 = 0, time.perf_counter()
+            while True:
+                oracle.scan_segmented_backward(qh, kh, vh, gh, ho[:n + 1], scale)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return done * H * int(ho[n]) / dt, (f"{done} pass(es) over the first {n} sequences "
+                                                 f"({int(ho[n])} tokens x {H} heads)")
         b.cpu = cpu
         return b
 
@@ -502,7 +546,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
                     choices=["single", "dense", "long_bf16", "ragged", "stream", "append",
-                             "reduce", "backward", "self_attn", "layer", "mean_query", "copy"])
+                             "reduce", "backward", "ragged_backward", "self_attn", "layer",
+                             "mean_query", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle time budget for cpu_baseline (0 to skip)")
     args = ap.parse_args()

@@ -34,6 +34,7 @@ EXPORTS = (
     "aaren_self_attention_workspace_size", "aaren_self_attention", "aaren_scan_strided",
     "aaren_layer_workspace_size", "aaren_layer_forward",
     "aaren_mean_query_attention_workspace_size", "aaren_mean_query_attention",
+    "aaren_scan_segmented_backward_workspace_size", "aaren_scan_segmented_backward",
 )
 
 
@@ -67,6 +68,9 @@ def _load():
         "aaren_scan_strided": (I, [P, P, P, P, P, I64, I64, I64, I64, P, P, F, I, I, P, SZ, P]),
         "aaren_layer_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_mean_query_attention_workspace_size": (SZ, [I64, I64, I64, I64]),
+        "aaren_scan_segmented_backward_workspace_size": (SZ, [I64, I64, I64, I64]),
+        "aaren_scan_segmented_backward": (I, [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, F,
+                                              I, P, SZ, P]),
         "aaren_mean_query_attention": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
         "aaren_layer_forward": (I, [P, P, P, P, I64, I64, I64, I64, I64, F, I, P, SZ, P]),
         "aaren_self_attention": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, I, P, SZ, P]),
@@ -383,6 +387,35 @@ def aaren_layer_forward(x, w_kv, q, scale=None, out_dtype=None, out=None, worksp
                                    0 if ws is None else ws.numel() * ws.element_size(),
                                    _stream(dev)))
     return out
+
+
+def aaren_scan_segmented_backward_workspace_size(num_seqs, total_tokens, H, d) -> int:
+    return int(lib.aaren_scan_segmented_backward_workspace_size(num_seqs, total_tokens, H, d))
+
+
+def aaren_scan_segmented_backward(q, k, v, o, dout, lse, offsets, scale=None, dq=None, dk=None,
+                                  dv=None, workspace=None):
+    """Gradients of the packed scan: q [H,d]; k, v, o, dout [T,H,d] float32;
+    lse [T,H] from aaren_scan_segmented; offsets int64 [S+1] -> (dq, dk, dv)."""
+    dev = _need_cuda(q, k, v, o, dout, lse, offsets, dq, dk, dv, workspace)
+    T, H, d = k.shape
+    for t in (v, o, dout):
+        if t.shape != k.shape:
+            raise ValueError("k, v, o, dout must share one [T,H,d] shape")
+    if lse.shape != (T, H) or offsets.dtype != torch.int64 or offsets.dim() != 1:
+        raise ValueError("expected lse [T,H] and int64 offsets [S+1]")
+    S = offsets.numel() - 1
+    dq = dq if dq is not None else torch.empty(H, d, device=dev)
+    dk = dk if dk is not None else torch.empty_like(k)
+    dv = dv if dv is not None else torch.empty_like(v)
+    need = aaren_scan_segmented_backward_workspace_size(S, T, H, d)
+    ws = workspace if workspace is not None else _workspace("segbwd", need, dev, True)
+    _check(lib.aaren_scan_segmented_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(offsets), _ptr(dq), _ptr(dk),
+        _ptr(dv), S, T, H, d, default_scale(d) if scale is None else float(scale),
+        _dtype_code(k.dtype), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(dev)))
+    return dq, dk, dv
 
 
 def aaren_mean_query_attention_workspace_size(B, H, N, d) -> int:

@@ -406,6 +406,12 @@ AAREN_API aaren_status aaren_scan_backward(const void *q, const void *k, const v
     p.streams = B * H;
     p.H = H;
     p.N = N;
+    p.batch_stride = H * N * d;
+    p.head_stride = N * d;
+    p.row_stride = d;
+    p.lse_batch_stride = H * N;
+    p.lse_head_stride = N;
+    p.lse_row_stride = 1;
     p.chunks = chunks;
     p.group = kGroupDense;
     p.chunks_padded = (uint32_t)chunks_padded;
@@ -422,7 +428,122 @@ AAREN_API aaren_status aaren_scan_backward(const void *q, const void *k, const v
         fprintf(stderr, "[aaren] scan_backward B=%lld H=%lld N=%lld d=%lld tiles=%lld\n",
                 (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles);
     CHECK(prepare_counters(workspace, counter_bytes(B * H), st));
-    return hip_status(aaren::launch_scan_backward(p, (int)d, st), "scan backward launch");
+    return hip_status(aaren::launch_scan_backward(p, (int)d, false, st), "scan backward launch");
+}
+
+// ---- backward of the packed scan -------------------------------------------------
+
+AAREN_API size_t aaren_scan_segmented_backward_workspace_size(int64_t num_seqs,
+                                                              int64_t total_tokens, int64_t H,
+                                                              int64_t d)
+{
+    if (num_seqs < 0 || total_tokens < 0 || H < 0 || (d != 64 && d != 128))
+        return 0;
+    const int64_t tiles = mul_checked({H, ceil_div(total_tokens, aaren::backward_tile_rows((int)d))});
+    if (tiles < 0)
+        return 0;
+    const int64_t words = ceil_div(total_tokens, 32) + 1;
+    return aaren::kHeaderBytes + counter_bytes(H) + aaren::round256((size_t)words * 4) +
+           backward_slots_bytes(tiles, d) + aaren::round256((size_t)tiles * d * 4);
+}
+
+AAREN_API aaren_status aaren_scan_segmented_backward(
+    const void *q, const void *k, const void *v, const void *o, const void *dout,
+    const float *lse, const int64_t *offsets, float *dq, float *dk, float *dv, int64_t num_seqs,
+    int64_t total_tokens, int64_t H, int64_t d, float scale, aaren_dtype in_dtype,
+    void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    const int64_t T = total_tokens;
+    if (num_seqs < 0 || T < 0 || H < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (num_seqs %lld, T %lld, H %lld)",
+                    (long long)num_seqs, (long long)T, (long long)H);
+    CHECK(check_common(d, in_dtype, AAREN_F32));
+    if (in_dtype != AAREN_F32)
+        return fail(AAREN_ERR_UNSUPPORTED, "the backward pass takes float32 tensors");
+    const int64_t elems = mul_checked({T, H, d});
+    if (elems < 0 || mul_checked({H, d}) < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "T*H*d overflows");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (elems == 0) {  // no rows: dq is an empty sum
+        if (H * d == 0)
+            return AAREN_OK;
+        CHECK(check_ptr(dq, "dq"));
+        return hip_status(aaren::launch_fill_zero(dq, (size_t)(H * d) * 4, st), "dq clear launch");
+    }
+    if (num_seqs == 0)
+        return fail(AAREN_ERR_INVALID_ARG, "tokens but no sequences");
+    CHECK(check_ptr(q, "q"));
+    CHECK(check_ptr(k, "k"));
+    CHECK(check_ptr(v, "v"));
+    CHECK(check_ptr(o, "o"));
+    CHECK(check_ptr(dout, "dout"));
+    CHECK(check_ptr(dq, "dq"));
+    CHECK(check_ptr(dk, "dk"));
+    CHECK(check_ptr(dv, "dv"));
+    if (!lse || !offsets)
+        return fail(AAREN_ERR_INVALID_ARG, "lse or offsets is NULL");
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(offsets) & 7u))
+        return fail(AAREN_ERR_ALIGNMENT, "lse or offsets is misaligned");
+    const int64_t rows = aaren::backward_tile_rows((int)d);
+    const int64_t chunks = ceil_div(T, rows);
+    const int64_t tiles = H * chunks;
+    const int64_t chunks_padded = ceil_div(chunks, kGroupPacked) * kGroupPacked;
+    if (H * chunks_padded >= 0x7fffffff)
+        return fail(AAREN_ERR_UNSUPPORTED, "%lld tiles exceed the 2^31-1 launch limit",
+                    (long long)tiles);
+    const size_t need = aaren_scan_segmented_backward_workspace_size(num_seqs, T, H, d);
+    if (!workspace || workspace_bytes < need)
+        return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    need);
+    if (!aligned16(workspace))
+        return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const int64_t words = ceil_div(T, 32) + 1;  // one spare word: flags look one row ahead
+    uint32_t *bitmap = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes + counter_bytes(H));
+    const size_t bitmap_bytes = aaren::round256((size_t)words * 4);
+    aaren::BackwardParams p{};
+    p.q = static_cast<const float *>(q);
+    p.k = static_cast<const float *>(k);
+    p.v = static_cast<const float *>(v);
+    p.o = static_cast<const float *>(o);
+    p.g = static_cast<const float *>(dout);
+    p.lse = lse;
+    p.dk = dk;
+    p.dv = dv;
+    p.dq = dq;
+    p.streams = H;
+    p.H = H;
+    p.N = T;
+    p.batch_stride = 0;
+    p.head_stride = d;
+    p.row_stride = H * d;
+    p.lse_batch_stride = 0;
+    p.lse_head_stride = 1;
+    p.lse_row_stride = H;
+    p.bitmap = bitmap;
+    p.bitmap_words = words;
+    p.chunks = chunks;
+    p.group = kGroupPacked;
+    p.chunks_padded = (uint32_t)chunks_padded;
+    p.num_tiles = (uint32_t)tiles;
+    p.epoch = next_epoch();
+    p.scale = scale;
+    p.qscale = scale * 1.44269504088896340736f;
+    p.header = reinterpret_cast<uint32_t *>(ws);
+    p.counters = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes);
+    p.slots = reinterpret_cast<uint64_t *>(ws + aaren::kHeaderBytes + counter_bytes(H) +
+                                           bitmap_bytes);
+    p.dq_partial = reinterpret_cast<float *>(ws + aaren::kHeaderBytes + counter_bytes(H) +
+                                             bitmap_bytes + backward_slots_bytes(tiles, d));
+    if (log_enabled())
+        fprintf(stderr, "[aaren] scan_segmented_backward S=%lld T=%lld H=%lld d=%lld tiles=%lld\n",
+                (long long)num_seqs, (long long)T, (long long)H, (long long)d, (long long)tiles);
+    CHECK(prepare_counters(workspace, counter_bytes(H), st));
+    CHECK(hip_status(aaren::launch_segment_flags(offsets, num_seqs, T, bitmap, words, st),
+                     "segment flags launch"));
+    return hip_status(aaren::launch_scan_backward(p, (int)d, true, st),
+                      "segmented scan backward launch");
 }
 
 // ---- segmented scan -------------------------------------------------------------

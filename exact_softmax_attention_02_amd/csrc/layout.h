@@ -141,9 +141,15 @@ struct BackwardParams {
     float *dv;
     float *dq_partial;       // [H][B][chunks][D], one per tile
     float *dq;               // [H][D]
-    int64_t streams;         // B*H
+    int64_t streams;         // B*H (dense) or H (packed)
     int64_t H;
-    int64_t N;
+    int64_t N;               // rows per stream: N (dense) or T (packed)
+    // elements to row r of stream b*H + h, shared by q-side tensors k, v, o,
+    // dout, dk, dv: b * batch_stride + h * head_stride + r * row_stride
+    int64_t batch_stride, head_stride, row_stride;
+    int64_t lse_batch_stride, lse_head_stride, lse_row_stride;
+    const uint32_t *bitmap;  // sequence starts, one bit per row (packed only)
+    int64_t bitmap_words;
     int64_t chunks;
     uint32_t group;
     uint32_t chunks_padded;
@@ -172,6 +178,6 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams &p, int D, aaren_dtype in, aaren_dtype out,
                          hipStream_t stream);
 int reduce_rows_per_iteration(int D, aaren_dtype in);
-hipError_t launch_scan_backward(const BackwardParams &p, int D, hipStream_t stream);
+hipError_t launch_scan_backward(const BackwardParams &p, int D, bool segmented, hipStream_t stream);
 
 }  // namespace aaren

@@ -18,7 +18,11 @@
 //
 // One HBM pass: K, V, O, dO read and dK, dV written once (plus 4 bytes of L
 // per row); each tile leaves one partial dq, summed per head in a fixed order
-// by a second kernel, so dq is reproducible bit for bit.
+// by a second kernel, so dq is reproducible bit for bit. Packed batches
+// (one stream per head over all tokens) restart the suffix at every sequence
+// end.
+#include <type_traits>
+
 #include "lookback.h"
 
 namespace aaren {
@@ -38,7 +42,13 @@ struct BackwardShape {
 
 // Five row tensors per lane: without a bound the compiler keeps values in
 // AGPRs and runs one wave per SIMD; three waves fit without spilling.
-template <int D>
+//
+// SEG (packed batches): a row that ends its sequence (the next row starts
+// one) takes nothing from the rows after it, so the suffix state restarts
+// there. Groups and tiles carry a flag "holds a sequence end"; folding a
+// flagged state onto what follows keeps the flagged state alone, exactly as
+// the forward's flag-lifted combine does for sequence starts.
+template <int D, bool SEG>
 __global__ __launch_bounds__(64 * BackwardShape<D>::WAVES)
 __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const BackwardParams p)
 {
@@ -49,6 +59,8 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
 
     __shared__ uint32_t sh_chunk;
     __shared__ float sh_gm[NG], sh_gu[NG];
+    __shared__ uint32_t sh_gf[NG];
+    __shared__ uint32_t sh_last_end;
     __shared__ __attribute__((aligned(16))) float sh_gw[NG][D];
     __shared__ float sh_cm, sh_cu;
     __shared__ __attribute__((aligned(16))) float sh_cw[D];
@@ -75,11 +87,28 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
     }
     const int64_t chunk = p.chunks - 1 - ticket, stream = stream32;
     const int64_t tile = chunk * p.streams + stream;
+    const int64_t bat = stream / p.H, head = stream - bat * p.H;
     const int64_t row0 = chunk * ROWS + (int64_t)grp * R;
     const int64_t left = p.N - row0;
     const int nvalid = left <= 0 ? 0 : (left >= R ? R : (int)left);
 
-    const int64_t base = (stream * p.N + row0) * D;  // column 0 of the group's first row
+    // column 0 of the group's first row; rows are row_stride apart
+    const int64_t base = bat * p.batch_stride + head * p.head_stride + row0 * p.row_stride;
+    const int64_t rs = p.row_stride;
+
+    // bit r: row r of the group ends its sequence (row r + 1 starts one)
+    uint32_t ends = 0;
+    if constexpr (SEG) {
+        if (nvalid > 0) {
+            const int64_t wi = (row0 + 1) >> 5;
+            const int sh = (int)((row0 + 1) & 31);
+            uint64_t bits = wi < p.bitmap_words ? p.bitmap[wi] : 0u;
+            if (wi + 1 < p.bitmap_words)
+                bits |= (uint64_t)p.bitmap[wi + 1] << 32;
+            ends = (uint32_t)(bits >> sh) & ((1u << nvalid) - 1u);
+        }
+    }
+
     // dO and O first: the tile's aggregate needs only them and L, so it is
     // published (and the look-back chain moves on) before K and V arrive
     u32x4 gr[R], orr[R];
@@ -87,14 +116,16 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
     for (int r = 0; r < R; ++r) {
         gr[r] = orr[r] = u32x4{0, 0, 0, 0};
         if (r < nvalid) {
-            gr[r] = load_slice<D, float, true>(p.g + base + r * D, gl);
-            orr[r] = load_slice<D, float, true>(p.o + base + r * D, gl);
+            gr[r] = load_slice<D, float, true>(p.g + base + r * rs, gl);
+            orr[r] = load_slice<D, float, true>(p.o + base + r * rs, gl);
         }
     }
     float lm[R];  // leaf exponent -L_r, log2 units
+    const float *lse_row = p.lse + bat * p.lse_batch_stride + head * p.lse_head_stride +
+                           row0 * p.lse_row_stride;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        lm[r] = (r < nvalid) ? -p.lse[stream * p.N + row0 + r] * kLog2e : kNegInf;
+        lm[r] = (r < nvalid) ? -lse_row[r * p.lse_row_stride] * kLog2e : kNegInf;
 
     // delta_r = <g_r, o_r>
     float dl[R];
@@ -110,18 +141,20 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
         dl[r] = group_sum<L>(b);
     }
 
-    // ---- pass 1: the group's suffix aggregate, maximum first ------------------
+    // ---- pass 1: the group's suffix aggregate from its first row, up to its
+    // first sequence end (packed), maximum first -------------------------------
+    const int last = (SEG && ends) ? __builtin_ctz(ends) : R - 1;
     float gm = kNegInf;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        gm = fmaxf(gm, lm[r]);
+        gm = (r <= last) ? fmaxf(gm, lm[r]) : gm;
     float gu = 0.f, gwv[E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
         gwv[e] = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const float f = (r < nvalid) ? exp2_fast(lm[r] - gm) : 0.f;
+        const float f = (r < nvalid && r <= last) ? exp2_fast(lm[r] - gm) : 0.f;
         float gf[E];
         widen<float>(gr[r], gf);
         gu = __builtin_fmaf(f, dl[r], gu);
@@ -135,6 +168,9 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
     if (gl == 0) {
         sh_gm[grp] = gm;
         sh_gu[grp] = gu;
+        sh_gf[grp] = ends != 0;
+        if (grp == NG - 1)
+            sh_last_end = (ends >> (R - 1)) & 1u;  // the tile's last row ends a sequence
     }
     // K and V land during the barrier and the look-back (O's registers are free)
     u32x4 kr[R], vr[R];
@@ -142,60 +178,84 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
     for (int r = 0; r < R; ++r) {
         kr[r] = vr[r] = u32x4{0, 0, 0, 0};
         if (r < nvalid)
-            kr[r] = load_slice<D, float, true>(p.k + base + r * D, gl);
+            kr[r] = load_slice<D, float, true>(p.k + base + r * rs, gl);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
         if (r < nvalid)
-            vr[r] = load_slice<D, float, true>(p.v + base + r * D, gl);
+            vr[r] = load_slice<D, float, true>(p.v + base + r * rs, gl);
     __syncthreads();
 
+    // fold a group state G onto X (the rows after it): G (+) X, or G alone if
+    // G holds a sequence end
+    auto fold_group = [&](int g, float &xm, float &xu, float *xw, bool &xf, auto col) {
+        constexpr int NE = decltype(col)::value == 0 ? E : CPL;
+        float yw[NE];
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            yw[e] = sh_gw[g][decltype(col)::value == 0 ? SL::col(gl, e) : lane + 64 * e];
+        if (SEG && sh_gf[g]) {
+            xm = sh_gm[g];
+            xu = sh_gu[g];
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                xw[e] = yw[e];
+            xf = true;
+        } else {
+            combine<NE>(sh_gm[g], sh_gu[g], yw, xm, xu, xw, xm, xu, xw);
+        }
+    };
+    using SliceCols = std::integral_constant<int, 0>;
+    using LaneCols = std::integral_constant<int, 1>;
+
     // state of the groups after this one in the tile: G_{g+1} (+) ... (+) G_{NG-1}
-    auto later_groups = [&](float &xm, float &xu, float *xw) {
+    auto later_groups = [&](float &xm, float &xu, float *xw, bool &xf) {
         xm = kNegInf;
         xu = 0.f;
+        xf = false;
 #pragma unroll
         for (int e = 0; e < E; ++e)
             xw[e] = 0.f;
-        for (int g = NG - 1; g > grp; --g) {
-            float yw[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                yw[e] = sh_gw[g][SL::col(gl, e)];
-            combine<E>(sh_gm[g], sh_gu[g], yw, xm, xu, xw, xm, xu, xw);
-        }
+        for (int g = NG - 1; g > grp; --g)
+            fold_group(g, xm, xu, xw, xf, SliceCols{});
     };
 
     float pm, pu, pw[E];
+    bool pf;
     if (wave != 0)
-        later_groups(pm, pu, pw);
+        later_groups(pm, pu, pw, pf);
 
     if (wave == 0) {
         // tile aggregate, column-per-lane, folded from the last group
         float am = kNegInf, au = 0.f, aw[CPL];
+        bool af = false;
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
             aw[c] = 0.f;
-        for (int g = NG - 1; g >= 0; --g) {
-            float yw[CPL];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c)
-                yw[c] = sh_gw[g][lane + 64 * c];
-            combine<CPL>(sh_gm[g], sh_gu[g], yw, am, au, aw, am, au, aw);
-        }
+        for (int g = NG - 1; g >= 0; --g)
+            fold_group(g, am, au, aw, af, LaneCols{});
         uint64_t *my = p.slots + (size_t)tile * 2 * SLOT;
         float cm = kNegInf, cu = 0.f, cw[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
             cw[c] = 0.f;
-        if (chunk < p.chunks - 1) {
-            publish<D>(my, epoch << 1, am, au, aw, lane);
-            // the carry is A_{j+1} (+) ... (+) A_last, the stream's later aggregates
-            lookback<D, false, true>(p.slots, tile + p.streams, p.streams, p.num_tiles, epoch,
-                                     lane, p.header, sh_win, cm, cu, cw);
+        // the carry is needed unless this is the stream's last tile or the
+        // tile's last row ends a sequence
+        const bool need_carry = chunk < p.chunks - 1 && !(SEG && sh_last_end);
+        if (need_carry) {
+            publish<D>(my, (epoch << 1) | (af ? 1u : 0u), am, au, aw, lane);
+            // the carry is A_{j+1} (+) ... (+) A_last, the stream's later
+            // aggregates (up to the next sequence end, packed batches)
+            lookback<D, SEG, true>(p.slots, tile + p.streams, p.streams, p.num_tiles, epoch,
+                                   lane, p.header, sh_win, cm, cu, cw);
         }
-        float im, iu, iw[CPL];
-        combine<CPL>(am, au, aw, cm, cu, cw, im, iu, iw);
+        // inclusive suffix = aggregate (+) carry, unless the tile holds an end
+        float im = am, iu = au, iw[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            iw[c] = aw[c];
+        if (!af)
+            combine<CPL>(am, au, aw, cm, cu, cw, im, iu, iw);
         publish<D>(my + SLOT, epoch << 1, im, iu, iw, lane);
         if (lane == 0) {
             sh_cm = cm;
@@ -204,13 +264,13 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
             sh_cw[lane + 64 * c] = cw[c];
-        later_groups(pm, pu, pw);
+        later_groups(pm, pu, pw, pf);
     }
     __syncthreads();
 
     // scores, log2 units
     float qv[E], qs[E];
-    widen<float>(load_slice<D, float, false>(p.q + (stream % p.H) * D, gl), qv);
+    widen<float>(load_slice<D, float, false>(p.q + head * D, gl), qv);
 #pragma unroll
     for (int e = 0; e < E; ++e)
         qs[e] = qv[e] * p.qscale;
@@ -227,8 +287,11 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
     }
 
     // ---- pass 2: rows last-first from (later groups (+) carry) ----------------
-    float xm, xu, xw[E];
-    {
+    float xm = pm, xu = pu, xw[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        xw[e] = pw[e];
+    if (!pf) {
         float cw[E];
 #pragma unroll
         for (int e = 0; e < E; ++e)
@@ -242,6 +305,13 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
 #pragma unroll
     for (int r = R - 1; r >= 0; --r) {
         if (r < nvalid) {
+            if (SEG && ((ends >> r) & 1u)) {  // the rows after this one belong to another sequence
+                xm = kNegInf;
+                xu = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    xw[e] = 0.f;
+            }
             float gf[E], vf[E], kf[E];
             widen<float>(gr[r], gf);
             widen<float>(vr[r], vf);
@@ -262,8 +332,8 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
                 dk[e] = sds * qv[e];
                 dq_acc[e] = __builtin_fmaf(sds, kf[e], dq_acc[e]);
             }
-            store_slice<D, float, float>(p.dv + base + r * D, gl, dv);
-            store_slice<D, float, float>(p.dk + base + r * D, gl, dk);
+            store_slice<D, float, float>(p.dv + base + r * rs, gl, dv);
+            store_slice<D, float, float>(p.dk + base + r * rs, gl, dk);
         }
     }
 
@@ -276,7 +346,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
     if (wave == 0) {
         // partials of one head are contiguous: [H][B][chunks][D]
         const int64_t B = p.streams / p.H;
-        const int64_t at = ((stream % p.H) * B + stream / p.H) * p.chunks + chunk;
+        const int64_t at = (head * B + bat) * p.chunks + chunk;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             float acc = 0.f;
@@ -324,10 +394,16 @@ __global__ __launch_bounds__(kDqThreads) void scan_backward_dq_kernel(const Back
 }
 
 template <int D>
-static hipError_t backward_one(const BackwardParams &p, hipStream_t stream)
+static hipError_t backward_one(const BackwardParams &p, bool segmented, hipStream_t stream)
 {
-    hipLaunchKernelGGL((scan_backward_kernel<D>), dim3((unsigned)(p.streams * p.chunks_padded)),
-                       dim3(64 * BackwardShape<D>::WAVES), 0, stream, p);
+    if (segmented)
+        hipLaunchKernelGGL((scan_backward_kernel<D, true>),
+                           dim3((unsigned)(p.streams * p.chunks_padded)),
+                           dim3(64 * BackwardShape<D>::WAVES), 0, stream, p);
+    else
+        hipLaunchKernelGGL((scan_backward_kernel<D, false>),
+                           dim3((unsigned)(p.streams * p.chunks_padded)),
+                           dim3(64 * BackwardShape<D>::WAVES), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -336,9 +412,11 @@ static hipError_t backward_one(const BackwardParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_scan_backward(const BackwardParams &p, int D, hipStream_t stream)
+hipError_t launch_scan_backward(const BackwardParams &p, int D, bool segmented,
+                                hipStream_t stream)
 {
-    return D == 64 ? backward_one<64>(p, stream) : backward_one<128>(p, stream);
+    return D == 64 ? backward_one<64>(p, segmented, stream)
+                   : backward_one<128>(p, segmented, stream);
 }
 
 }  // namespace aaren

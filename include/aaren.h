@@ -202,6 +202,25 @@ aaren_status aaren_append(const void *q, const void *k, const void *v,
                           int64_t S, int64_t T, int64_t H, int64_t d, float scale,
                           aaren_dtype in_dtype, aaren_dtype out_dtype, void *hip_stream);
 
+/* ---- backward of the packed scan -------------------------------------------
+ * Gradients of aaren_scan_segmented (float32): each sequence's gradients are
+ * those of a dense scan of that sequence alone; dq adds every sequence's.
+ *   q [H,d]; k, v, o, dout [T,H,d] token-major; lse [T,H] (aaren_scan_segmented's
+ *   lse output); offsets [num_seqs+1] int64 device array as for the forward;
+ *   dq [H,d], dk, dv [T,H,d] float32 outputs.
+ * Workspace as for aaren_scan_backward (zero-filled once before first use;
+ * size from the query). T = 0: dq is zeroed, OK. Tokens with num_seqs = 0:
+ * INVALID_ARG. offsets must be 8-byte aligned. */
+size_t aaren_scan_segmented_backward_workspace_size(int64_t num_seqs, int64_t total_tokens,
+                                                    int64_t H, int64_t d);
+aaren_status aaren_scan_segmented_backward(const void *q, const void *k, const void *v,
+                                           const void *o, const void *dout, const float *lse,
+                                           const int64_t *offsets, float *dq, float *dk,
+                                           float *dv, int64_t num_seqs, int64_t total_tokens,
+                                           int64_t H, int64_t d, float scale,
+                                           aaren_dtype in_dtype, void *workspace,
+                                           size_t workspace_bytes, void *hip_stream);
+
 /* ---- many-to-one reduction -------------------------------------------------
  * Single-query attention over all N pairs ("Self-attention Does Not Need
  * O(n^2) Memory", sections 1-2; "Attention as an RNN", abstract item (1):

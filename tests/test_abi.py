@@ -196,6 +196,22 @@ def test_mean_query_validation():
     assert aaren.aaren_mean_query_attention_workspace_size(1, 2, 100, 96) == 0
 
 
+def test_segmented_backward_validation():
+    sb = lambda **kw: L.aaren_scan_segmented_backward(
+        A, A, A, A, A, kw.get("lse", A), kw.get("offs", A), A, A, A, kw.get("S_", 3),
+        kw.get("T", 100), 2, 64, 0.125, kw.get("inp", 0), kw.get("ws", A), kw.get("wsb", 1 << 24),
+        None)
+    assert sb(inp=1) == S["unsup"]          # float32 only
+    assert sb(S_=0) == S["arg"]             # tokens but no sequences
+    assert sb(lse=0) == S["arg"]
+    assert sb(offs=A + 4) == S["align"]
+    assert sb(wsb=64) == S["ws"]
+    assert sb(T=-1) == S["arg"]
+    # header + 2 counters + bitmap (T/32 + 1 words) + 2 states per tile + dq partials
+    assert aaren.aaren_scan_segmented_backward_workspace_size(3, 1000, 2, 64) == \
+        256 + 256 + 256 + 2 * 8 * 2 * 72 * 8 + 2 * 8 * 64 * 4
+
+
 def test_reduce_validation():
     rd = lambda **kw: L.aaren_reduce(A, A, A, A, kw.get("m", None), None, 1, 1, kw.get("N", 10),
                                      64, 0.125, 0, 0, kw.get("ws", A), kw.get("wsb", 1 << 20), None)

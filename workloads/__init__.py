@@ -60,6 +60,10 @@ WORKLOADS = {
     # packed variable-length batch
     "ragged": Workload("ragged", "segmented", dict(num_seqs=4096, max_len=8192, H=8, d=64),
                        "f32", 4),
+    # gradients of a packed batch a quarter the size of the ragged one (the
+    # six gradient-pass tensors of the full one would need ~210 GB)
+    "ragged_backward": Workload("ragged_backward", "segmented",
+                                dict(num_seqs=1024, max_len=8192, H=8, d=64), "f32", 10),
     # many independent streams, one token appended per call
     "stream": Workload("stream", "step", dict(S=262144, H=4, d=64, steps=256), "f32", 5),
     # the same streams and tokens, 16 tokens appended per call
