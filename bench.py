@@ -593,7 +593,11 @@ def main():
     if args.cpu_seconds > 0 and b.cpu is not None:
         import oracle
         rate, sample = b.cpu(args.cpu_seconds)
-        cores = oracle.threads() if args.workload not in ("reduce", "mean_query") else 1
+        cores = oracle.threads()
+        if args.workload in ("reduce", "mean_query"):
+            cores = 1  # one unit: the recurrence runs on one thread
+        elif args.workload == "ragged_backward":
+            cores = min(cores, b.config["H"])  # each sequence's heads are its parallel units
         cpu = {"value": rate, "unit": b.unit, "cores": cores, "kind": "oracle", "sample": sample}
 
     line = {

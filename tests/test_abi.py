@@ -227,3 +227,18 @@ def test_workspace_clear_validation():
     assert L.aaren_workspace_clear(A + 3, 64, None) == S["align"]
     assert L.aaren_workspace_clear(0, 64, None) == S["arg"]
     assert L.aaren_workspace_clear(0, 0, None) == 0
+
+
+def test_header_is_plain_c99(tmp_path):
+    """include/aaren.h compiles as C99 with no HIP or C++ headers around it,
+    and its prototypes agree with a C caller taking every entry point's
+    address."""
+    import subprocess
+    names = declared_functions()
+    src = tmp_path / "use.c"
+    src.write_text('#include "aaren.h"\n#include <stddef.h>\ntypedef void (*fn)(void);\n'
+                   "const fn table[] = {\n" + ",\n".join(f"  (fn)&{n}" for n in names) +
+                   "\n};\nint main(void) { return table[0] == NULL; }\n")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
+                        "-I", os.path.dirname(HEADER), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
