@@ -164,7 +164,7 @@ extern "C" aaren_status aaren_layer_fail(aaren_status s, const char *msg)
 
 AAREN_API int aaren_version(void)
 {
-    return 100;  // 0.1.0
+    return 200;  // 0.2.0
 }
 
 AAREN_API const char *aaren_status_string(aaren_status s)

@@ -4,7 +4,11 @@
  * The library computes attention of ONE query per head over a sequence of
  * key/value pairs, and its many-to-many form, through the associative
  * online-softmax combine of a running maximum m, a normaliser u and a
- * weighted value sum w.
+ * weighted value sum w: the prefix scan (dense, strided and packed), its
+ * gradients, the per-token and multi-token constant-memory updates and the
+ * many-to-one reduction; and, built on the same combine, self-attention with
+ * one query per token, one Aaren layer (projections + scan) and attention of
+ * a mean query.
  *
  * Sources (the pages these calls implement):
  *  - "Self-attention Does Not Need O(n^2) Memory" (review), section 1
@@ -28,9 +32,12 @@
  *
  * Conventions:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing and keeps no pointer after a call's work completes.
- *  - Tensors are dense, row-major, in the shapes given; q, k and v share
- *    `in_dtype`; every tensor base pointer must be 16-byte aligned.
+ *    allocates nothing (one exception: the first aaren_layer_forward call on
+ *    a device creates a rocBLAS handle, which allocates once) and keeps no
+ *    pointer after a call's work completes.
+ *  - Tensors are dense, row-major, in the shapes given (aaren_scan_strided
+ *    takes explicit strides); q, k and v share `in_dtype` unless a call says
+ *    otherwise; every tensor base pointer must be 16-byte aligned.
  *  - d (head dimension) is 64 or 128.
  *  - `hip_stream` is a hipStream_t (NULL = the null stream). Every call only
  *    enqueues work on that stream and returns; device-side faults surface at

@@ -40,7 +40,7 @@ def test_binding_has_the_same_names():
 
 
 def test_version_and_strings():
-    assert aaren.aaren_version() == 100
+    assert aaren.aaren_version() == 200
     for st in range(6):
         assert aaren.aaren_status_string(st)
     assert aaren.aaren_status_string(99) == "unknown status"
