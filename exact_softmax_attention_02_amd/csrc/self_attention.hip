@@ -191,9 +191,13 @@ __global__ __launch_bounds__(64 * kAttnWaves, 8 / kAttnWaves) void self_attentio
             for (int r = 0; r < 16; ++r)
                 tx = fmaxf(tx, (!EDGE || key_off(t, r) < lim) ? s[t][r] : kNegInf);
         tx = fmaxf(tx, __shfl_xor(tx, 32));
-        // a lane whose keys are all masked has tx = -inf; with a zero scale
-        // tx * c2 is NaN, and fmaxf keeps m
-        const float mnew = fmaxf(m, tx * c2);
+        // The maximum is moved only when a score exceeds it by more than 2^8
+        // (log2 units): the weights then stay below 256, harmless in fp32 and
+        // in the bf16 hi/lo split, and the rescale of O (and its register
+        // traffic) is skipped on most tiles. The quotient does not depend on
+        // the reference. A lane whose keys are all masked has tx = -inf; with a
+        // zero scale tx * c2 is NaN and the comparison keeps m.
+        const float mnew = (tx * c2 > m + 8.f) ? tx * c2 : m;
         const float alpha = exp2_fast(m - mnew);  // 0 on the first tile (m = -inf)
         m = mnew;
         lsum *= alpha;
