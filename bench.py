@@ -403,7 +403,7 @@ def make(name: str, device):
         b.config = {"workload": f"self-attention, one query per token {b.describe}", "B": B, "H": H,
                     "N": N, "d": d, "causal": causal, "in_dtype": "bf16", "out_dtype": "f32",
                     "flops_per_call": b.flops_per_launch}
-        b.kernel = "self_attention_kernel (+ attn_transpose_kernel)"
+        b.kernel = "self_attention_kernel (+ attn_vmax_kernel, attn_transpose_kernel)"
 
         def cpu(budget_s):
             import oracle

@@ -763,7 +763,9 @@ AAREN_API size_t aaren_self_attention_workspace_size(int64_t B, int64_t H, int64
     const int64_t elems = mul_checked({B, H, d, aaren::attn_padded_keys(N)});
     if (elems < 0)
         return 0;
-    return aaren::round256((size_t)elems * 2);
+    // [V^T fp16][partial maxima of |V|, uint32 per (b,h) and part]
+    return aaren::round256((size_t)elems * 2) +
+           aaren::round256((size_t)(B * H) * aaren::kAttnVmaxParts * 4);
 }
 
 AAREN_API aaren_status aaren_self_attention(const void *q, const void *k, const void *v, void *o,
@@ -805,6 +807,9 @@ AAREN_API aaren_status aaren_self_attention(const void *q, const void *k, const 
     p.k = static_cast<const uint16_t *>(k);
     p.v = static_cast<const uint16_t *>(v);
     p.vt = static_cast<uint16_t *>(workspace);
+    p.vmax = reinterpret_cast<uint32_t *>(
+        static_cast<uint8_t *>(workspace) +
+        aaren::round256((size_t)mul_checked({B, H, d, aaren::attn_padded_keys(N)}) * 2));
     p.o = o;
     p.lse = lse;
     p.bh = B * H;

@@ -24,11 +24,16 @@ __host__ __device__ constexpr int64_t attn_padded_keys(int64_t N)
     return (N + kAttnKeys - 1) / kAttnKeys * kAttnKeys;
 }
 
+// V's largest magnitude per (b,h) is reduced in this many partial maxima,
+// which one wave combines.
+constexpr int kAttnVmaxParts = 64;
+
 struct AttnParams {
     const uint16_t *q;   // bf16 bits [BH][N][D]
     const uint16_t *k;   // bf16 bits [BH][N][D]
     const uint16_t *v;   // bf16 bits [BH][N][D]
-    uint16_t *vt;        // workspace: bf16 bits [BH][D][Np], V transposed, zero past N
+    uint16_t *vt;        // workspace: fp16 bits [BH][D][Np], 2^e(b,h) V transposed, zero past N
+    uint32_t *vmax;      // workspace: [BH][kAttnVmaxParts] partial max |v| (bf16 bits)
     void *o;             // [BH][N][D], float or bf16
     float *lse;          // [BH][N] or null, natural units
     int64_t bh;          // B*H

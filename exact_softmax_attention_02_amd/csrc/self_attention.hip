@@ -22,9 +22,15 @@
 //  * V^T must present 8 consecutive keys of one dimension per lane; V is
 //    transposed once into the workspace by a pre-pass, so its tiles load
 //    into LDS as plain rows.
-//  * P is carried to ~15 significant bits as bf16 hi + bf16 lo (two MFMAs per
-//    step): rounding P to bf16 alone would move outputs by up to ~2^-9 |v|,
-//    the whole budget of the bf16 tolerance. The normaliser sums P in fp32.
+//  * The value product runs in fp16 (v_mfma_f32_32x32x16_f16), whose 11
+//    significant bits move an output by at most ~2^-12 max|v| where bf16's 8
+//    would take ~2^-9 max|v|, the whole budget of the bf16 tolerance. V is
+//    multiplied per (b,h) by a power of two 2^e that brings its largest
+//    magnitude just under 2^15 (so every bf16 value of V at or above 2^-17 of
+//    that scale converts exactly), and the output by 2^-e. The weights are
+//    taken as 2^7 e^{s - m}: with the running maximum moved only by more than
+//    2^8 they stay below 2^15, and only weights under 2^-21 of the maximum
+//    fall into fp16's subnormals. The normaliser sums the weights in fp32.
 #include <type_traits>
 
 #include "device.h"
@@ -33,6 +39,9 @@
 namespace aaren {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(1))) void *gptr;
@@ -43,14 +52,85 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
 }
 
-// V [BH][N][D] -> V^T [BH][D][Np], zero for keys N..Np-1. One workgroup per
-// 64 keys x 64 dimensions.
+__device__ __forceinline__ f32x16 mfma32h(u32x4 a, f16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), b, c, 0, 0, 0);
+}
+
+// Partial maxima of the finite |v| over [BH][N][D], as bf16 magnitude bits
+// (which order like the magnitudes; infinities and NaNs are left out, so they
+// do not set the scale): part c of head bh covers keys [c*len, (c+1)*len),
+// len = ceil(N / kAttnVmaxParts).
+template <int D>
+__global__ __launch_bounds__(256) void attn_vmax_kernel(const AttnParams p)
+{
+    __shared__ uint32_t red[4];
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int64_t len = (p.N + kAttnVmaxParts - 1) / kAttnVmaxParts;
+    int64_t k0 = blockIdx.x * len, k1 = k0 + len;
+    k1 = k1 < p.N ? k1 : p.N;
+    k0 = k0 < k1 ? k0 : k1;
+    const uint16_t *src = p.v + (bh * p.N + k0) * D;
+    const int64_t chunks = (k1 - k0) * (D / 8);  // 16-byte chunks
+    uint32_t mx = 0;
+    for (int64_t c = tid; c < chunks; c += 256) {
+        const u32x4 x = load16(src + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t a = x[e] & 0x7fffu, b = (x[e] >> 16) & 0x7fffu;
+            a = a < 0x7f80u ? a : 0u;
+            b = b < 0x7f80u ? b : 0u;
+            mx = mx > a ? mx : a;
+            mx = mx > b ? mx : b;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)mx, off);
+        mx = mx > o ? mx : o;
+    }
+    if ((tid & 63) == 0)
+        red[tid >> 6] = mx;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t r = red[0];
+        for (int w = 1; w < 4; ++w)
+            r = r > red[w] ? r : red[w];
+        p.vmax[bh * kAttnVmaxParts + blockIdx.x] = r;
+    }
+}
+
+// The exponent e of head bh's value scale 2^e, from its partial maxima (one
+// wave reads them all): the largest finite |v| < 2^(E - 126) for bf16
+// exponent field E <= 254, so e = 141 - E >= -113 puts it below 2^15. Capped
+// at 126 (zero or subnormal V). Infinities and NaNs stay what they are.
+__device__ __forceinline__ int attn_value_exponent(const AttnParams &p, int64_t bh, int lane)
+{
+    uint32_t mx = p.vmax[bh * kAttnVmaxParts + lane];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)mx, off);
+        mx = mx > o ? mx : o;
+    }
+    const int E = (int)(mx >> 7);
+    return 141 - E < 126 ? 141 - E : 126;
+}
+
+__device__ __forceinline__ float pow2f(int e)  // 2^e for -126 <= e <= 127
+{
+    return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+// V [BH][N][D] bf16 -> 2^e V^T [BH][D][Np] fp16 (rounded to nearest), zero
+// for keys N..Np-1. One workgroup per 64 keys x 64 dimensions.
 template <int D>
 __global__ __launch_bounds__(256) void attn_transpose_kernel(const AttnParams p)
 {
     __shared__ uint16_t t[64][64 + 2];  // [key][dim]
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.z, key0 = (int64_t)blockIdx.x * 64, dim0 = blockIdx.y * 64;
+    const float vscale = pow2f(attn_value_exponent(p, bh, tid & 63));
     for (int c = tid; c < 512; c += 256) {
         const int key = c / 8, ch = c % 8;
         u32x4 x = {0, 0, 0, 0};
@@ -58,8 +138,11 @@ __global__ __launch_bounds__(256) void attn_transpose_kernel(const AttnParams p)
             x = load16(p.v + ((bh * p.N + key0 + key) * D + dim0 + 8 * ch));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            t[key][8 * ch + 2 * e] = (uint16_t)(x[e] & 0xffffu);
-            t[key][8 * ch + 2 * e + 1] = (uint16_t)(x[e] >> 16);
+            const f32x2 f = {__uint_as_float(x[e] << 16) * vscale,
+                             __uint_as_float(x[e] & 0xffff0000u) * vscale};
+            const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+            t[key][8 * ch + 2 * e] = (uint16_t)(h & 0xffffu);
+            t[key][8 * ch + 2 * e + 1] = (uint16_t)(h >> 16);
         }
     }
     __syncthreads();
@@ -191,12 +274,12 @@ __global__ __launch_bounds__(64 * kAttnWaves, 8 / kAttnWaves) void self_attentio
             for (int r = 0; r < 16; ++r)
                 tx = fmaxf(tx, (!EDGE || key_off(t, r) < lim) ? s[t][r] : kNegInf);
         tx = fmaxf(tx, __shfl_xor(tx, 32));
-        // The maximum is moved only when a score exceeds it by more than 2^8
-        // (log2 units): the weights then stay below 256, harmless in fp32 and
-        // in the bf16 hi/lo split, and the rescale of O (and its register
-        // traffic) is skipped on most tiles. The quotient does not depend on
-        // the reference. A lane whose keys are all masked has tx = -inf; with a
-        // zero scale tx * c2 is NaN and the comparison keeps m.
+        // The maximum is moved only when a score exceeds it by more than 8
+        // (log2 units): the weights then stay below 2^8 (2^15 with the 2^7
+        // offset), and the rescale of O (and its register traffic) is skipped
+        // on most tiles. The quotient does not depend on the reference. A lane
+        // whose keys are all masked has tx = -inf; with a zero scale tx * c2 is
+        // NaN and the comparison keeps m.
         const float mnew = (tx * c2 > m + 8.f) ? tx * c2 : m;
         const float alpha = exp2_fast(m - mnew);  // 0 on the first tile (m = -inf)
         m = mnew;
@@ -206,7 +289,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, 8 / kAttnWaves) void self_attentio
             for (int dt = 0; dt < DT; ++dt)
                 oacc[dt] *= alpha;
         }
-        // O^T += V^T P^T, 16 keys per step, P as bf16 hi + lo
+        // O^T += V^T P^T, 16 keys per step, P = 2^7 e^{s - m} in fp16
+        const float mk = mnew - 7.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -214,74 +298,80 @@ __global__ __launch_bounds__(64 * kAttnWaves, 8 / kAttnWaves) void self_attentio
                 f32x8 pe;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    pe[e] = exp2_fast(__builtin_fmaf(s[t][8 * s2 + e], c2, -mnew));
+                    pe[e] = exp2_fast(__builtin_fmaf(s[t][8 * s2 + e], c2, -mk));
                     if (EDGE && key_off(t, 8 * s2 + e) >= lim)
                         pe[e] = 0.f;
                     lsum += pe[e];
                 }
-                // hi: the upper 16 bits of each float (truncation, error < 2^-7 p);
-                // lo: the remainder rounded to bf16, so hi + lo is within 2^-15 p
-                u32x4 hp;
-                f32x8 hf;
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const uint32_t a = __float_as_uint(pe[e]), b = __float_as_uint(pe[e + 1]);
-                    hp[e / 2] = (a >> 16) | (b & 0xffff0000u);
-                    hf[e] = __uint_as_float(a & 0xffff0000u);
-                    hf[e + 1] = __uint_as_float(b & 0xffff0000u);
-                }
-                const bf16x8 ph = __builtin_bit_cast(bf16x8, hp);
-                const bf16x8 pl = __builtin_convertvector(pe - hf, bf16x8);
+                const f16x8 ph = __builtin_convertvector(pe, f16x8);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     const int vr = 32 * dt + l32;
                     const u32x4 a = load16(&sv[buf][vr * kAttnKeys +
                                                     8 * ((4 * t + 2 * s2 + h32) ^ vswz(vr))]);
-                    oacc[dt] = mfma32(a, ph, oacc[dt]);
-                    oacc[dt] = mfma32(a, pl, oacc[dt]);
+                    oacc[dt] = mfma32h(a, ph, oacc[dt]);
                 }
             }
         }
     };
 
-    for (int j = 0; j < ntiles; ++j) {
+    // tiles 0..nfull-1 need no mask: every key is below N and, causal, below
+    // every query of the workgroup
+    int64_t nfull = p.N / kAttnKeys;
+    if (p.causal && (q0 + 1) / kAttnKeys < nfull)
+        nfull = (q0 + 1) / kAttnKeys;
+    int j = 0;
+    for (; j < (int)nfull; ++j) {
         const int buf = j & 1;
         if (j + 1 < ntiles)
             load_tile(j + 1, buf ^ 1);  // that buffer was last read before the previous barrier
-        const int64_t k0 = (int64_t)j * kAttnKeys;
-        if (k0 + kAttnKeys > p.N || (p.causal && k0 + kAttnKeys - 1 > q0)) {
-            int64_t lim = p.N - k0;
-            if (p.causal && qi + 1 - k0 < lim)
-                lim = qi + 1 - k0;
-            tile(buf, lim < 0 ? 0 : (lim > kAttnKeys ? kAttnKeys : (int)lim),
-                 std::integral_constant<bool, true>{});
-        } else {
-            tile(buf, kAttnKeys, std::integral_constant<bool, false>{});
-        }
+        tile(buf, kAttnKeys, std::integral_constant<bool, false>{});
         __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
+        __syncthreads();
+    }
+    for (; j < ntiles; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < ntiles)
+            load_tile(j + 1, buf ^ 1);
+        const int64_t k0 = (int64_t)j * kAttnKeys;
+        int64_t lim = p.N - k0;
+        if (p.causal && qi + 1 - k0 < lim)
+            lim = qi + 1 - k0;
+        tile(buf, lim < 0 ? 0 : (lim > kAttnKeys ? kAttnKeys : (int)lim),
+             std::integral_constant<bool, true>{});
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
     lsum += __shfl_xor(lsum, 32);
+    const float vdescale = pow2f(-attn_value_exponent(p, bh, lane));
     if (qi < p.N) {
+        // divide first, then undo V's scale: for a tiny V the result may be
+        // subnormal, and only the last product rounds into that range
         const float inv = 1.f / lsum;
+        auto out = [&](float x) { return x * inv * vdescale; };
         Tout *orow = static_cast<Tout *>(p.o) + (bh * p.N + qi) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                store4<Tout>(orow + 32 * dt + 8 * g + 4 * h32, oacc[dt][4 * g] * inv,
-                             oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
-                             oacc[dt][4 * g + 3] * inv);
+                store4<Tout>(orow + 32 * dt + 8 * g + 4 * h32, out(oacc[dt][4 * g]),
+                             out(oacc[dt][4 * g + 1]), out(oacc[dt][4 * g + 2]),
+                             out(oacc[dt][4 * g + 3]));
         }
         if (p.lse && h32 == 0)
-            p.lse[bh * p.N + qi] = (m + log2_fast(lsum)) * kLn2;
+            p.lse[bh * p.N + qi] = (m + (log2_fast(lsum) - 7.f)) * kLn2;
     }
 }
 
 template <int D>
 static hipError_t attention_one(const AttnParams &p, aaren_dtype out, hipStream_t stream)
 {
+    hipLaunchKernelGGL((attn_vmax_kernel<D>), dim3((unsigned)kAttnVmaxParts, (unsigned)p.bh),
+                       dim3(256), 0, stream, p);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess)
+        return e0;
     hipLaunchKernelGGL((attn_transpose_kernel<D>),
                        dim3((unsigned)(p.Np / 64), (unsigned)(D / 64), (unsigned)p.bh), dim3(256),
                        0, stream, p);

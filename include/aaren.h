@@ -277,12 +277,18 @@ aaren_status aaren_layer_forward(const void *x, const void *w_kv, const float *q
  *   q, k, v [B,H,N,d] bfloat16 (in_dtype must be AAREN_BF16);
  *   o [B,H,N,d] (out_dtype F32 or BF16);
  *   lse [B,H,N] float32 or NULL: L_i = ln sum_j e^{s_ij} (natural units).
- * Scores and the value sums are accumulated in fp32 on the matrix cores;
- * the softmax weights enter the value sum with 16 significant bits.
+ * Scores (bf16 products) and the value sums are accumulated in fp32 on the
+ * matrix cores. The value product takes the softmax weights and V in fp16
+ * (11 significant bits): V is first multiplied per (b,h) by the power of two
+ * that brings its largest finite magnitude just under 2^15, which is exact
+ * for every value at or above 2^-17 of that scale, and the output is
+ * multiplied back. An output then lies within about 2^-12 max|v| of exact
+ * (max over the row's keys). Infinities and NaNs in V give non-finite
+ * outputs in their dimension.
  * The workspace (size from the query; no zero-fill needed, every call
- * overwrites what it reads) holds V transposed. B*H*N = 0: OK, nothing
- * is read or written. Statuses as for aaren_scan; UNSUPPORTED also for
- * float32 inputs and for B*H > 65535. */
+ * overwrites what it reads) holds the scaled V transposed and the per-(b,h)
+ * magnitude maxima. B*H*N = 0: OK, nothing is read or written. Statuses as
+ * for aaren_scan; UNSUPPORTED also for float32 inputs and for B*H > 65535. */
 size_t aaren_self_attention_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d);
 aaren_status aaren_self_attention(const void *q, const void *k, const void *v, void *o,
                                   float *lse, int64_t B, int64_t H, int64_t N, int64_t d,

@@ -149,7 +149,8 @@ def test_self_attention_validation():
     assert sa(ws=A + 8) == S["align"]
     assert L.aaren_self_attention(0, 0, 0, 0, None, 1, 2, 0, 64, 0.125, 1, 1, 0, 0, 0, None) == 0
     # V transposed, keys padded to a multiple of 64, bf16
-    assert aaren.aaren_self_attention_workspace_size(2, 3, 100, 64) == 2 * 3 * 64 * 128 * 2
+    # V^T in fp16 (keys padded to 128), then 64 uint32 partial maxima per (b,h)
+    assert aaren.aaren_self_attention_workspace_size(2, 3, 100, 64) == 2 * 3 * 64 * 128 * 2 + 6 * 64 * 4
     assert aaren.aaren_self_attention_workspace_size(1, 1, 10, 100) == 0
 
 

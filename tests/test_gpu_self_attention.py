@@ -80,3 +80,29 @@ def test_empty_and_reproducible():
     a = aaren.aaren_self_attention(q, k, v)
     for _ in range(3):
         assert torch.equal(a, aaren.aaren_self_attention(q, k, v))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_value_magnitudes(d):
+    """Values far outside fp16's range, per head: 2^40, 2^-40, bf16
+    subnormals (2^-130), unit scale, and unit scale with one element at 2^20.
+    The value product runs in fp16 after a power-of-two scale per (b,h);
+    attention is linear in V, so o / s is held to the unit-scale bound."""
+    announce(f"self-attention value magnitudes d={d}")
+    B, H, N = 1, 5, 333
+    q, k, _ = inputs(B, H, N, d, seed=13)
+    g = torch.Generator(device=dev()).manual_seed(14)
+    s = torch.tensor([2.0 ** 40, 2.0 ** -40, 2.0 ** -130, 1.0, 1.0], dtype=torch.float64)
+    v32 = torch.randn(B, H, N, d, generator=g, device=dev())
+    v32 = v32 * s.to(torch.float32).to(dev())[None, :, None, None]
+    v32[0, 4, 100, 7] = 2.0 ** 20
+    v = v32.to(torch.bfloat16).contiguous()
+    assert 0 < float(v[0, 2].float().abs().max()) < 2.0 ** -126  # subnormal head
+    scale = float(np.float32(d ** -0.5))
+    for causal in (True, False):
+        o = host32(aaren.aaren_self_attention(q, k, v, scale, causal=causal)).astype(np.float64)
+        ref = oracle.self_attention(host32(q), host32(k), host32(v), scale, causal=causal)
+        sn = s.numpy()[None, :, None, None]
+        err = oracle.max_scaled_err(o / sn, ref / sn)
+        assert err <= TOL[torch.bfloat16], (causal, err)
+        print(f"value magnitudes d={d} causal={causal}: o/s {err:.2e}")
