@@ -12,6 +12,7 @@ already resident in HBM:
   append                   : aaren_state_init + 16 aaren_append calls of 16
                              tokens, the same 256 tokens per stream
   backward                 : one aaren_scan_backward call on the dense batch
+  backward_bf16            : the same with bf16 q, K, V and output gradients
   ragged_backward          : one aaren_scan_segmented_backward call on a packed
                              batch of 1024 sequences
   mean_query               : one aaren_mean_query_attention call (keys/s)
@@ -142,21 +143,27 @@ def make(name: str, device):
         b.cpu = None
         return b
 
-    if name == "backward":
-        # gradients of the dense batch: the forward's o and lse are inputs
+    if name in ("backward", "backward_bf16"):
+        # gradients of the dense batch: the forward's o and lse are inputs;
+        # bf16: q, k, v and the output gradient in bf16, o and lse float32
         B, H, N, d = z["B"], z["H"], z["N"], z["d"]
-        q, k, v = wl.dense_inputs(B, H, N, d, w.seed, device=device)
+        q, k, v = wl.dense_inputs(B, H, N, d, w.seed, device=device, dtype=w.dtype)
         scale = wl.default_scale(d)
         o, lse = aaren.aaren_scan(q, k, v, scale, return_lse=True)
         g = torch.randn(B, H, N, d, device=device,
                         generator=torch.Generator(device=device).manual_seed(w.seed + 100))
+        g = g.to(k.dtype)
         dq = torch.empty(H, d, device=device)
         ws = torch.zeros(aaren.aaren_scan_backward_workspace_size(B, H, N, d), dtype=torch.uint8,
                          device=device)
-        b.bytes_per_launch = 6 * k.numel() * 4 + lse.numel() * 4 + dq.numel() * 4
+        # k, v, dout in their dtype; o read and dk, dv written in float32
+        b.bytes_per_launch = (3 * k.numel() * k.element_size() + 3 * k.numel() * 4 +
+                              lse.numel() * 4 + dq.numel() * 4)
         b.sets = n_sets(b.bytes_per_launch)
-        bufs = [(k, v, o, g, lse, torch.empty_like(k), torch.empty_like(v))]
-        bufs += [tuple(x.clone() for x in bufs[0][:5]) + (torch.empty_like(k), torch.empty_like(v))
+        f32 = torch.float32
+        bufs = [(k, v, o, g, lse, torch.empty_like(k, dtype=f32), torch.empty_like(v, dtype=f32))]
+        bufs += [tuple(x.clone() for x in bufs[0][:5]) +
+                 (torch.empty_like(k, dtype=f32), torch.empty_like(v, dtype=f32))
                  for _ in range(b.sets - 1)]
         turn = [0]
 
@@ -170,12 +177,12 @@ def make(name: str, device):
         b.units = B * H * N
         b.launches_per_step = 1
         b.config = {"workload": f"gradients of the dense many-to-many scan {b.describe}", "B": B,
-                    "H": H, "N": N, "d": d, "in_dtype": "f32", "out_dtype": "f32"}
+                    "H": H, "N": N, "d": d, "in_dtype": w.dtype, "out_dtype": "f32"}
         b.kernel = "scan_backward_kernel + scan_backward_dq_kernel"
 
         def cpu(budget_s):
             import oracle
-            qh, kh, vh, gh = (t.cpu().numpy() for t in (q, k, v, g))
+            qh, kh, vh, gh = (t.float().cpu().numpy() for t in (q, k, v, g))
             done, t0 = 0, time.perf_counter()
             while True:
                 oracle.scan_backward(qh, kh, vh, gh, scale)
@@ -546,7 +553,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
                     choices=["single", "dense", "long_bf16", "ragged", "stream", "append",
-                             "reduce", "backward", "ragged_backward", "self_attn", "layer",
+                             "reduce", "backward", "backward_bf16", "ragged_backward",
+                             "self_attn", "layer",
                              "mean_query", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle time budget for cpu_baseline (0 to skip)")

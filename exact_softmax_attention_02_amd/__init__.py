@@ -245,27 +245,34 @@ def aaren_scan_backward_workspace_size(B, H, N, d) -> int:
     return int(lib.aaren_scan_backward_workspace_size(B, H, N, d))
 
 
+def _backward_dtypes(q, k, v, o, dout, lse):
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype) or \
+            k.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q, k, v and dout must share one dtype, float32 or bfloat16")
+    if o.dtype != torch.float32 or lse.dtype != torch.float32:
+        raise TypeError("o and lse must be float32 (the forward's float32 outputs)")
+
+
 def aaren_scan_backward(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None,
                         workspace=None):
     """Gradients of the dense many-to-many scan: (dq [H,d], dk, dv [B,H,N,d]),
-    float32, from the forward's o and lse and the output gradient dout."""
+    float32, from the forward's o and lse and the output gradient dout. q, k,
+    v and dout share one dtype (float32 or bfloat16); o and lse are float32."""
     dev = _need_cuda(q, k, v, o, dout, lse, dq, dk, dv, workspace)
     B, H, N, d = k.shape
-    for t in (q, k, v, o, dout, lse):
-        if t.dtype != torch.float32:
-            raise TypeError("the backward pass takes float32 tensors")
+    _backward_dtypes(q, k, v, o, dout, lse)
     if q.shape != (H, d) or not (v.shape == o.shape == dout.shape == k.shape) or \
             lse.shape != (B, H, N):
         raise ValueError("expected q [H,d], k, v, o, dout [B,H,N,d] and lse [B,H,N]")
     dq = torch.empty(H, d, dtype=torch.float32, device=dev) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev) if dv is None else dv
     need = aaren_scan_backward_workspace_size(B, H, N, d)
     ws = workspace if workspace is not None else _workspace("scan", need, dev, True)
     _check(lib.aaren_scan_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                    _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
                                    default_scale(d) if scale is None else float(scale),
-                                   AAREN_F32, _ptr(ws),
+                                   _dtype_code(k.dtype), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(),
                                    _stream(dev)))
     return dq, dk, dv
@@ -395,10 +402,12 @@ def aaren_scan_segmented_backward_workspace_size(num_seqs, total_tokens, H, d) -
 
 def aaren_scan_segmented_backward(q, k, v, o, dout, lse, offsets, scale=None, dq=None, dk=None,
                                   dv=None, workspace=None):
-    """Gradients of the packed scan: q [H,d]; k, v, o, dout [T,H,d] float32;
-    lse [T,H] from aaren_scan_segmented; offsets int64 [S+1] -> (dq, dk, dv)."""
+    """Gradients of the packed scan: q [H,d]; k, v, dout [T,H,d] (float32 or
+    bfloat16, one dtype); o [T,H,d] and lse [T,H] float32 from
+    aaren_scan_segmented; offsets int64 [S+1] -> (dq, dk, dv) float32."""
     dev = _need_cuda(q, k, v, o, dout, lse, offsets, dq, dk, dv, workspace)
     T, H, d = k.shape
+    _backward_dtypes(q, k, v, o, dout, lse)
     for t in (v, o, dout):
         if t.shape != k.shape:
             raise ValueError("k, v, o, dout must share one [T,H,d] shape")
@@ -406,8 +415,8 @@ def aaren_scan_segmented_backward(q, k, v, o, dout, lse, offsets, scale=None, dq
         raise ValueError("expected lse [T,H] and int64 offsets [S+1]")
     S = offsets.numel() - 1
     dq = dq if dq is not None else torch.empty(H, d, device=dev)
-    dk = dk if dk is not None else torch.empty_like(k)
-    dv = dv if dv is not None else torch.empty_like(v)
+    dk = dk if dk is not None else torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = dv if dv is not None else torch.empty(v.shape, dtype=torch.float32, device=dev)
     need = aaren_scan_segmented_backward_workspace_size(S, T, H, d)
     ws = workspace if workspace is not None else _workspace("segbwd", need, dev, True)
     _check(lib.aaren_scan_segmented_backward(

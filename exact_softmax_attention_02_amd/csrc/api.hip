@@ -353,9 +353,7 @@ AAREN_API aaren_status aaren_scan_backward(const void *q, const void *k, const v
     if (B < 0 || H < 0 || N < 0)
         return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
                     (long long)B, (long long)H, (long long)N);
-    CHECK(check_common(d, in_dtype, AAREN_F32));
-    if (in_dtype != AAREN_F32)
-        return fail(AAREN_ERR_UNSUPPORTED, "the backward pass takes float32 tensors");
+    CHECK(check_common(d, in_dtype, AAREN_F32));  // q, k, v, dout: float32 or bf16
     const int64_t elems = mul_checked({B, H, N, d});
     if (elems < 0 || mul_checked({H, d}) < 0)
         return fail(AAREN_ERR_UNSUPPORTED, "B*H*N*d overflows");
@@ -394,11 +392,11 @@ AAREN_API aaren_status aaren_scan_backward(const void *q, const void *k, const v
 
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     aaren::BackwardParams p{};
-    p.q = static_cast<const float *>(q);
-    p.k = static_cast<const float *>(k);
-    p.v = static_cast<const float *>(v);
+    p.q = q;
+    p.k = k;
+    p.v = v;
     p.o = static_cast<const float *>(o);
-    p.g = static_cast<const float *>(dout);
+    p.g = dout;
     p.lse = lse;
     p.dk = dk;
     p.dv = dv;
@@ -428,7 +426,8 @@ AAREN_API aaren_status aaren_scan_backward(const void *q, const void *k, const v
         fprintf(stderr, "[aaren] scan_backward B=%lld H=%lld N=%lld d=%lld tiles=%lld\n",
                 (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles);
     CHECK(prepare_counters(workspace, counter_bytes(B * H), st));
-    return hip_status(aaren::launch_scan_backward(p, (int)d, false, st), "scan backward launch");
+    return hip_status(aaren::launch_scan_backward(p, (int)d, false, in_dtype, st),
+                      "scan backward launch");
 }
 
 // ---- backward of the packed scan -------------------------------------------------
@@ -457,9 +456,7 @@ AAREN_API aaren_status aaren_scan_segmented_backward(
     if (num_seqs < 0 || T < 0 || H < 0)
         return fail(AAREN_ERR_INVALID_ARG, "negative size (num_seqs %lld, T %lld, H %lld)",
                     (long long)num_seqs, (long long)T, (long long)H);
-    CHECK(check_common(d, in_dtype, AAREN_F32));
-    if (in_dtype != AAREN_F32)
-        return fail(AAREN_ERR_UNSUPPORTED, "the backward pass takes float32 tensors");
+    CHECK(check_common(d, in_dtype, AAREN_F32));  // q, k, v, dout: float32 or bf16
     const int64_t elems = mul_checked({T, H, d});
     if (elems < 0 || mul_checked({H, d}) < 0)
         return fail(AAREN_ERR_UNSUPPORTED, "T*H*d overflows");
@@ -503,11 +500,11 @@ AAREN_API aaren_status aaren_scan_segmented_backward(
     uint32_t *bitmap = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes + counter_bytes(H));
     const size_t bitmap_bytes = aaren::round256((size_t)words * 4);
     aaren::BackwardParams p{};
-    p.q = static_cast<const float *>(q);
-    p.k = static_cast<const float *>(k);
-    p.v = static_cast<const float *>(v);
+    p.q = q;
+    p.k = k;
+    p.v = v;
     p.o = static_cast<const float *>(o);
-    p.g = static_cast<const float *>(dout);
+    p.g = dout;
     p.lse = lse;
     p.dk = dk;
     p.dv = dv;
@@ -542,7 +539,7 @@ AAREN_API aaren_status aaren_scan_segmented_backward(
     CHECK(prepare_counters(workspace, counter_bytes(H), st));
     CHECK(hip_status(aaren::launch_segment_flags(offsets, num_seqs, T, bitmap, words, st),
                      "segment flags launch"));
-    return hip_status(aaren::launch_scan_backward(p, (int)d, true, st),
+    return hip_status(aaren::launch_scan_backward(p, (int)d, true, in_dtype, st),
                       "segmented scan backward launch");
 }
 

@@ -131,11 +131,11 @@ __host__ __device__ constexpr int backward_tile_rows(int D)
 }
 
 struct BackwardParams {
-    const float *q;
-    const float *k;
-    const float *v;
-    const float *o;
-    const float *g;          // dloss/do
+    const void *q;           // q, k, v, g: float or bf16 (the call's in_dtype)
+    const void *k;
+    const void *v;
+    const float *o;          // the forward's output, float32
+    const void *g;           // dloss/do
     const float *lse;        // log-normaliser per row, natural units
     float *dk;
     float *dv;
@@ -178,6 +178,7 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams &p, int D, aaren_dtype in, aaren_dtype out,
                          hipStream_t stream);
 int reduce_rows_per_iteration(int D, aaren_dtype in);
-hipError_t launch_scan_backward(const BackwardParams &p, int D, bool segmented, hipStream_t stream);
+hipError_t launch_scan_backward(const BackwardParams &p, int D, bool segmented, aaren_dtype in,
+                                hipStream_t stream);
 
 }  // namespace aaren

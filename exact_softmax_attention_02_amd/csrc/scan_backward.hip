@@ -20,12 +20,43 @@
 // per row); each tile leaves one partial dq, summed per head in a fixed order
 // by a second kernel, so dq is reproducible bit for bit. Packed batches
 // (one stream per head over all tokens) restart the suffix at every sequence
-// end.
+// end. q, K, V and dO may be bf16 (widened exactly); O, L and the gradients
+// are float32.
 #include <type_traits>
 
 #include "lookback.h"
 
 namespace aaren {
+
+// A lane's 4 consecutive columns 4gl..4gl+3 of a row, raw: 16 bytes of fp32
+// or 8 bytes of bf16, and their exact float values.
+template <typename T>
+using RawCols = std::conditional_t<sizeof(T) == 4, u32x4, u32x2>;
+
+template <typename T, bool STREAM>
+__device__ __forceinline__ RawCols<T> load_cols(const T *row, int gl)
+{
+    if constexpr (sizeof(T) == 4) {
+        return STREAM ? load16_stream(row + 4 * gl) : load16(row + 4 * gl);
+    } else {
+        const u32x2 *a = reinterpret_cast<const u32x2 *>(row + 4 * gl);
+        return STREAM ? __builtin_nontemporal_load(a) : *a;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void widen_cols(RawCols<T> raw, float *out)
+{
+    if constexpr (sizeof(T) == 4) {
+        widen<float>(raw, out);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            out[2 * i] = __uint_as_float(raw[i] << 16);
+            out[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+        }
+    }
+}
 
 template <int D>
 struct BackwardShape {
@@ -48,10 +79,12 @@ struct BackwardShape {
 // there. Groups and tiles carry a flag "holds a sequence end"; folding a
 // flagged state onto what follows keeps the flagged state alone, exactly as
 // the forward's flag-lifted combine does for sequence starts.
-template <int D, bool SEG>
+template <int D, bool SEG, typename Tin>
 __global__ __launch_bounds__(64 * BackwardShape<D>::WAVES)
 __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const BackwardParams p)
 {
+    const Tin *pq = static_cast<const Tin *>(p.q), *pk = static_cast<const Tin *>(p.k);
+    const Tin *pv = static_cast<const Tin *>(p.v), *pg = static_cast<const Tin *>(p.g);
     using S = BackwardShape<D>;
     using SL = Slice<D, float>;
     constexpr int E = S::E, L = S::L, GPW = S::GPW, NG = S::NG, R = S::R, ROWS = S::ROWS;
@@ -111,13 +144,15 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
 
     // dO and O first: the tile's aggregate needs only them and L, so it is
     // published (and the look-back chain moves on) before K and V arrive
-    u32x4 gr[R], orr[R];
+    RawCols<Tin> gr[R];
+    u32x4 orr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        gr[r] = orr[r] = u32x4{0, 0, 0, 0};
+        gr[r] = RawCols<Tin>{};
+        orr[r] = u32x4{0, 0, 0, 0};
         if (r < nvalid) {
-            gr[r] = load_slice<D, float, true>(p.g + base + r * rs, gl);
-            orr[r] = load_slice<D, float, true>(p.o + base + r * rs, gl);
+            gr[r] = load_cols<Tin, true>(pg + base + r * rs, gl);
+            orr[r] = load_cols<float, true>(p.o + base + r * rs, gl);
         }
     }
     float lm[R];  // leaf exponent -L_r, log2 units
@@ -132,7 +167,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         float gf[E], of[E];
-        widen<float>(gr[r], gf);
+        widen_cols<Tin>(gr[r], gf);
         widen<float>(orr[r], of);
         float b = 0.f;
 #pragma unroll
@@ -156,7 +191,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
     for (int r = 0; r < R; ++r) {
         const float f = (r < nvalid && r <= last) ? exp2_fast(lm[r] - gm) : 0.f;
         float gf[E];
-        widen<float>(gr[r], gf);
+        widen_cols<Tin>(gr[r], gf);
         gu = __builtin_fmaf(f, dl[r], gu);
 #pragma unroll
         for (int e = 0; e < E; ++e)
@@ -173,17 +208,17 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
             sh_last_end = (ends >> (R - 1)) & 1u;  // the tile's last row ends a sequence
     }
     // K and V land during the barrier and the look-back (O's registers are free)
-    u32x4 kr[R], vr[R];
+    RawCols<Tin> kr[R], vr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        kr[r] = vr[r] = u32x4{0, 0, 0, 0};
+        kr[r] = vr[r] = RawCols<Tin>{};
         if (r < nvalid)
-            kr[r] = load_slice<D, float, true>(p.k + base + r * rs, gl);
+            kr[r] = load_cols<Tin, true>(pk + base + r * rs, gl);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
         if (r < nvalid)
-            vr[r] = load_slice<D, float, true>(p.v + base + r * rs, gl);
+            vr[r] = load_cols<Tin, true>(pv + base + r * rs, gl);
     __syncthreads();
 
     // fold a group state G onto X (the rows after it): G (+) X, or G alone if
@@ -270,7 +305,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
 
     // scores, log2 units
     float qv[E], qs[E];
-    widen<float>(load_slice<D, float, false>(p.q + head * D, gl), qv);
+    widen_cols<Tin>(load_cols<Tin, false>(pq + head * D, gl), qv);
 #pragma unroll
     for (int e = 0; e < E; ++e)
         qs[e] = qv[e] * p.qscale;
@@ -278,7 +313,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         float kf[E];
-        widen<float>(kr[r], kf);
+        widen_cols<Tin>(kr[r], kf);
         float a = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e)
@@ -313,9 +348,9 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
                     xw[e] = 0.f;
             }
             float gf[E], vf[E], kf[E];
-            widen<float>(gr[r], gf);
-            widen<float>(vr[r], vf);
-            widen<float>(kr[r], kf);
+            widen_cols<Tin>(gr[r], gf);
+            widen_cols<Tin>(vr[r], vf);
+            widen_cols<Tin>(kr[r], kf);
             combine<E>(lm[r], dl[r], gf, xm, xu, xw, xm, xu, xw);  // leaf (+) state
             const float pw_r = exp2_fast(s[r] + xm);  // e^{s_r} times the state's scale
             float dv[E], part = 0.f;
@@ -393,15 +428,15 @@ __global__ __launch_bounds__(kDqThreads) void scan_backward_dq_kernel(const Back
     }
 }
 
-template <int D>
+template <int D, typename Tin>
 static hipError_t backward_one(const BackwardParams &p, bool segmented, hipStream_t stream)
 {
     if (segmented)
-        hipLaunchKernelGGL((scan_backward_kernel<D, true>),
+        hipLaunchKernelGGL((scan_backward_kernel<D, true, Tin>),
                            dim3((unsigned)(p.streams * p.chunks_padded)),
                            dim3(64 * BackwardShape<D>::WAVES), 0, stream, p);
     else
-        hipLaunchKernelGGL((scan_backward_kernel<D, false>),
+        hipLaunchKernelGGL((scan_backward_kernel<D, false, Tin>),
                            dim3((unsigned)(p.streams * p.chunks_padded)),
                            dim3(64 * BackwardShape<D>::WAVES), 0, stream, p);
     hipError_t e = hipGetLastError();
@@ -412,11 +447,14 @@ static hipError_t backward_one(const BackwardParams &p, bool segmented, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_scan_backward(const BackwardParams &p, int D, bool segmented,
+hipError_t launch_scan_backward(const BackwardParams &p, int D, bool segmented, aaren_dtype in,
                                 hipStream_t stream)
 {
-    return D == 64 ? backward_one<64>(p, segmented, stream)
-                   : backward_one<128>(p, segmented, stream);
+    if (in == AAREN_BF16)
+        return D == 64 ? backward_one<64, bf16>(p, segmented, stream)
+                       : backward_one<128, bf16>(p, segmented, stream);
+    return D == 64 ? backward_one<64, float>(p, segmented, stream)
+                   : backward_one<128, float>(p, segmented, stream);
 }
 
 }  // namespace aaren

@@ -123,13 +123,14 @@ aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, fl
  *   dv_i = sum_{k>=i} p_ki g_k
  *   ds_i = <dv_i, v_i> - sum_{k>=i} p_ki <g_k, o_k>
  *   dk_i = scale ds_i q_h,  dq_h = scale sum_{b,i} ds_i k_i  (summed over the batch)
- *   q [H,d], k, v, o, dout [B,H,N,d]  float32 (o and lse from aaren_scan)
+ *   q [H,d], k, v, dout [B,H,N,d]  in_dtype (float32 or bfloat16)
+ *   o [B,H,N,d] float32: the forward's output (aaren_scan with out_dtype F32)
  *   lse [B,H,N] float32: the forward's log-normaliser
  *   dq [H,d], dk, dv [B,H,N,d] float32 outputs
- * One pass over K, V, O and dout; dq is reproducible bit for bit. in_dtype
- * must be AAREN_F32 (others: UNSUPPORTED). The workspace follows the scan
- * workspace contract (zero-filled once; may be shared with the scans). With
- * B*H*N == 0, dq is set to zero. */
+ * One pass over K, V, O and dout; dq is reproducible bit for bit. bfloat16
+ * inputs are widened exactly and everything after is float32 arithmetic. The
+ * workspace follows the scan workspace contract (zero-filled once; may be
+ * shared with the scans). With B*H*N == 0, dq is set to zero. */
 size_t aaren_scan_backward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d);
 aaren_status aaren_scan_backward(const void *q, const void *k, const void *v, const void *o,
                                  const void *dout, const float *lse,
@@ -210,10 +211,11 @@ aaren_status aaren_append(const void *q, const void *k, const void *v,
                           aaren_dtype in_dtype, aaren_dtype out_dtype, void *hip_stream);
 
 /* ---- backward of the packed scan -------------------------------------------
- * Gradients of aaren_scan_segmented (float32): each sequence's gradients are
- * those of a dense scan of that sequence alone; dq adds every sequence's.
- *   q [H,d]; k, v, o, dout [T,H,d] token-major; lse [T,H] (aaren_scan_segmented's
- *   lse output); offsets [num_seqs+1] int64 device array as for the forward;
+ * Gradients of aaren_scan_segmented: each sequence's gradients are those of
+ * a dense scan of that sequence alone; dq adds every sequence's.
+ *   q [H,d]; k, v, dout [T,H,d] token-major, in_dtype (float32 or bfloat16);
+ *   o [T,H,d] float32 and lse [T,H] (aaren_scan_segmented's outputs);
+ *   offsets [num_seqs+1] int64 device array as for the forward;
  *   dq [H,d], dk, dv [T,H,d] float32 outputs.
  * Workspace as for aaren_scan_backward (zero-filled once before first use;
  * size from the query). T = 0: dq is zeroed, OK. Tokens with num_seqs = 0:

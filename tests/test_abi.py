@@ -202,7 +202,7 @@ def test_segmented_backward_validation():
         A, A, A, A, A, kw.get("lse", A), kw.get("offs", A), A, A, A, kw.get("S_", 3),
         kw.get("T", 100), 2, 64, 0.125, kw.get("inp", 0), kw.get("ws", A), kw.get("wsb", 1 << 24),
         None)
-    assert sb(inp=1) == S["unsup"]          # float32 only
+    assert sb(inp=7) == S["unsup"]          # unknown dtype (float32 and bf16 are taken)
     assert sb(S_=0) == S["arg"]             # tokens but no sequences
     assert sb(lse=0) == S["arg"]
     assert sb(offs=A + 4) == S["align"]

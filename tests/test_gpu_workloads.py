@@ -129,14 +129,17 @@ def test_reduce_in_full():
     print(f"reduce: max scaled err {err:.3e}")
 
 
-def test_dense_gradients_in_full():
-    """Gradients at the dense batch's full size (the backward bench's shape)."""
-    w = W["dense"]
+@pytest.mark.parametrize("name", ["dense", "backward_bf16"])
+def test_dense_gradients_in_full(name):
+    """Gradients at the dense batch's full size (the backward benches' shape),
+    float32 and with bf16 q, K, V and output gradients."""
+    w = W[name]
     sz = w.sizes
     B, H, N, d = sz["B"], sz["H"], sz["N"], sz["d"]
-    announce(f"workload dense gradients: {w.describe()}")
-    q, k, v = workloads.dense_inputs(B, H, N, d, w.seed, device=dev())
+    announce(f"workload {name} gradients: {w.describe()}")
+    q, k, v = workloads.dense_inputs(B, H, N, d, w.seed, device=dev(), dtype=w.dtype)
     g = torch.randn(B, H, N, d, device=dev(), generator=torch.Generator(device=dev()).manual_seed(w.seed + 100))
+    g = g.to(k.dtype)
     scale = workloads.default_scale(d)
     o, lse = aaren.aaren_scan(q, k, v, scale, return_lse=True)
     dq, dk, dv = aaren.aaren_scan_backward(q, k, v, o, g, lse, scale)
@@ -153,7 +156,7 @@ def test_dense_gradients_in_full():
         per_term = (depth * 2.0 ** -24 + 1e-5) * sds + 1e-5 / abs(qh[h, j])
         bound = (per_term[..., None] * np.abs(kh[:, h])).sum(axis=(0, 1))
         assert np.all(np.abs(host32(dq[h]) - rq[h]) <= bound)
-    print(f"dense gradients: dk {e_k:.3e} dv {e_v:.3e}")
+    print(f"{name} gradients: dk {e_k:.3e} dv {e_v:.3e}")
 
 
 def test_stream_appends_sampled_streams():

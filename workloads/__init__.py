@@ -19,6 +19,9 @@ for them):
              default_rng(seed); K,V packed token-major [T,H,d], N(0,1).
 * stream:    q [H,d]; per append t, k_t and v_t [S,H,d] N(0,1).
 * reduce:    as dense with B = H = 1.
+* gradients: the forward's inputs as above; the output gradient dO is N(0,1)
+             from its own generator (seed + 100), rounded to bfloat16 for
+             bf16 inputs.
 
 The GPU draws (torch's Philox generator) differ from CPU draws for the same
 seed; a test always draws on one device and copies the exact bytes to the
@@ -57,6 +60,9 @@ WORKLOADS = {
     # long sequences, bf16 inputs, scores stretched to +-80
     "long_bf16": Workload("long_bf16", "dense", dict(B=4, H=16, N=65536, d=128), "bf16", 3,
                           score_span=80.0),
+    # gradients of the dense batch with bf16 q, K, V and output gradients
+    # (the forward's output and log-normaliser stay float32)
+    "backward_bf16": Workload("backward_bf16", "dense", dict(B=32, H=8, N=4096, d=64), "bf16", 2),
     # packed variable-length batch
     "ragged": Workload("ragged", "segmented", dict(num_seqs=4096, max_len=8192, H=8, d=64),
                        "f32", 4),
