@@ -28,9 +28,10 @@
 //    multiplied per (b,h) by a power of two 2^e that brings its largest
 //    magnitude just under 2^15 (so every bf16 value of V at or above 2^-17 of
 //    that scale converts exactly), and the output by 2^-e. The weights are
-//    taken as 2^7 e^{s - m}: with the running maximum moved only by more than
-//    2^8 they stay below 2^15, and only weights under 2^-21 of the maximum
-//    fall into fp16's subnormals. The normaliser sums the weights in fp32.
+//    taken as 2^7 e^{s - m}: the running maximum moves only when a score
+//    exceeds it by more than a factor 2^8, so they stay below 2^15, and only
+//    weights under 2^-21 of the maximum fall into fp16's subnormals. The
+//    normaliser sums the weights in fp32.
 #include <type_traits>
 
 #include "device.h"
