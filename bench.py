@@ -122,6 +122,33 @@ def measured_traffic(kind: str, workload: str):
             c["write_kib_per_dispatch"] * 1024 * c["copy_write_factor"])
 
 
+def input_checksums(inputs) -> dict:
+    """Per input tensor (or list of tensors): the sum of its raw words as signed
+    integers (32-bit words for fp32, 16-bit for bf16, 64-bit for int64), taken
+    on the device in int64 and reported modulo 2^64 in hex. Exact and order-free,
+    so it identifies the bytes a run used without copying them to the host."""
+    import torch
+    words = {8: torch.int64, 4: torch.int32, 2: torch.int16, 1: torch.int8}
+    out = {}
+    for name, t in inputs.items():
+        total = 0
+        for x in (t if isinstance(t, (list, tuple)) else [t]):
+            total += int(x.contiguous().view(words[x.element_size()]).sum(dtype=torch.int64))
+        out[name] = f"{total % (1 << 64):016x}"
+    return out
+
+
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 class Workload:
     """A prepared workload: step() runs one pass; the numbers describe it."""
     kind = "scan"
@@ -149,6 +176,7 @@ def make(name: str, device):
         # a plain device copy of known size (the dense batch's K): the practical
         # read+write ceiling, and the reference the HBM counters are scaled by
         x = torch.randn(32, 8, 4096, 64, device=device)
+        b.inputs = {"x": x}
         b.sets = n_sets(2 * x.numel() * 4)
         bufs = [(x, torch.empty_like(x))] + [(x.clone(), torch.empty_like(x))
                                              for _ in range(b.sets - 1)]
@@ -180,6 +208,7 @@ def make(name: str, device):
         g = torch.randn(B, H, N, d, device=device,
                         generator=torch.Generator(device=device).manual_seed(w.seed + 100))
         g = g.to(k.dtype)
+        b.inputs = dict(q=q, k=k, v=v, dout=g)
         dq = torch.empty(H, d, device=device)
         ws = torch.zeros(aaren.aaren_scan_backward_workspace_size(B, H, N, d), dtype=torch.uint8,
                          device=device)
@@ -230,6 +259,7 @@ def make(name: str, device):
         o, lse = aaren.aaren_scan_segmented(q, k, v, offs, scale, return_lse=True)
         g = torch.randn(T, H, d, device=device,
                         generator=torch.Generator(device=device).manual_seed(w.seed + 100))
+        b.inputs = dict(q=q, k=k, v=v, offsets=offs, dout=g)
         dq, dk, dv = torch.empty(H, d, device=device), torch.empty_like(k), torch.empty_like(v)
         ws = torch.zeros(aaren.aaren_scan_segmented_backward_workspace_size(len(lengths), T, H, d),
                          dtype=torch.uint8, device=device)
@@ -267,6 +297,7 @@ def make(name: str, device):
         B, H, N, d = z["B"], z["H"], z["N"], z["d"]
         q, k, v = wl.dense_inputs(B, H, N, d, w.seed, device=device, dtype=w.dtype,
                                   score_span=w.score_span)
+        b.inputs = dict(q=q, k=k, v=v)
         scale = wl.default_scale(d)
         o = torch.empty(B, H, N, d, device=device)
         ws = torch.zeros(aaren.aaren_scan_workspace_size(B, H, N, d), dtype=torch.uint8,
@@ -307,6 +338,7 @@ def make(name: str, device):
         H, d = z["H"], z["d"]
         lengths = wl.segment_lengths(z["num_seqs"], z["max_len"], w.seed)
         q, k, v, offs = wl.segmented_inputs(lengths, H, d, w.seed, device=device)
+        b.inputs = dict(q=q, k=k, v=v, offsets=offs)
         T = int(lengths.sum())
         scale = wl.default_scale(d)
         o = torch.empty(T, H, d, device=device)
@@ -342,6 +374,7 @@ def make(name: str, device):
     elif w.kind == "step":
         S, H, d, T = z["S"], z["H"], z["d"], z["steps"]
         q, k, v = wl.step_inputs(S, H, d, T, w.seed, device=device)
+        b.inputs = dict(q=q, k=k, v=v)
         scale = wl.default_scale(d)
         m, u, st_w = aaren.new_state(S, H, d, device=device)
         o = torch.empty(S, H, d, device=device)
@@ -380,6 +413,7 @@ def make(name: str, device):
     elif w.kind == "append":
         S, H, d, T, blk = z["S"], z["H"], z["d"], z["steps"], z["block"]
         q, k, v = wl.step_inputs(S, H, d, T, w.seed, device=device)
+        b.inputs = dict(q=q, k=k, v=v)
         scale = wl.default_scale(d)
         m, u, st_w = aaren.new_state(S, H, d, device=device)
         o = torch.empty(blk, S, H, d, device=device)
@@ -420,6 +454,7 @@ def make(name: str, device):
     elif w.kind == "self_attention":
         B, H, N, d, causal = z["B"], z["H"], z["N"], z["d"], bool(z["causal"])
         q, k, v = wl.self_attention_inputs(B, H, N, d, w.seed, device=device)
+        b.inputs = dict(q=q, k=k, v=v)
         scale = wl.default_scale(d)
         o = torch.empty(B, H, N, d, device=device)
         ws = torch.empty(aaren.aaren_self_attention_workspace_size(B, H, N, d), dtype=torch.uint8,
@@ -458,6 +493,7 @@ def make(name: str, device):
     elif w.kind == "mean_query":
         B, H, N, d = z["B"], z["H"], z["N"], z["d"]
         hq, k, v = wl.mean_query_inputs(B, H, N, d, w.seed, device=device)
+        b.inputs = dict(hq=hq, k=k, v=v)
         scale = wl.default_scale(d)
         o = torch.empty(B, H, d, device=device)
         ws = torch.empty(aaren.aaren_mean_query_attention_workspace_size(B, H, N, d),
@@ -495,6 +531,7 @@ def make(name: str, device):
     elif w.kind == "layer":
         B, N, Dm, H, d, L = z["B"], z["N"], z["Dm"], z["H"], z["d"], z["layers"]
         x, ws_, qs = wl.layer_inputs(B, N, Dm, H, d, L, w.seed, device=device)
+        b.inputs = dict(x=x, w_kv=ws_, q=qs)
         scale = wl.default_scale(d)
         bufs = [torch.empty(B, N, H, d, dtype=torch.bfloat16, device=device) for _ in range(2)]
         work = torch.zeros(aaren.aaren_layer_workspace_size(B, N, H, d), dtype=torch.uint8,
@@ -537,6 +574,7 @@ def make(name: str, device):
     else:  # reduce
         B, H, N, d = z["B"], z["H"], z["N"], z["d"]
         q, k, v = wl.reduce_inputs(B, H, N, d, w.seed, device=device)
+        b.inputs = dict(q=q, k=k, v=v)
         scale = wl.default_scale(d)
         o = torch.empty(B, H, d, device=device)
         ws = torch.empty(aaren.aaren_reduce_workspace_size(B, H, N, d), dtype=torch.uint8,
@@ -596,6 +634,7 @@ def main():
 
     device = torch.device("cuda:0")
     b = make(args.workload, device)
+    checksums = input_checksums(getattr(b, "inputs", {}))
     stream = torch.cuda.current_stream(device)
     for _ in range(args.warmup):
         b.step()
@@ -633,7 +672,8 @@ def main():
             cores = 1  # one unit: the recurrence runs on one thread
         elif args.workload == "ragged_backward":
             cores = min(cores, b.config["H"])  # each sequence's heads are its parallel units
-        cpu = {"value": rate, "unit": b.unit, "cores": cores, "kind": "oracle", "sample": sample}
+        cpu = {"value": rate, "unit": b.unit, "cores": cores, "kind": "oracle", "sample": sample,
+               "cpu_model": host_cpu(), "host_threads": os.cpu_count()}
 
     line = {
         "metric": "tokens/s and achieved HBM GB/s (% of peak) for aaren_scan at B*H*N, d=64/128"
@@ -649,7 +689,7 @@ def main():
         "vs_baseline": None,
         "dtype": b.dtype,
         "data": "synthetic (seeded i.i.d. normal inputs; no dataset)",
-        "config": dict(b.config, input_sets=b.sets,
+        "config": dict(b.config, input_sets=b.sets, input_checksums=checksums,
                        note=("steps rotate over input copies so that each step reads HBM"
                              if b.sets > 1 else "one input set")),
         "achieved_GBps": achieved,
