@@ -379,10 +379,26 @@ def make(name: str, device):
         m, u, st_w = aaren.new_state(S, H, d, device=device)
         o = torch.empty(S, H, d, device=device)
 
+        # events every T/8 appends (the last step's are kept): the time per
+        # append must not grow with t, the state being constant-size
+        seg = max(1, T // 8)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(T // seg + 1)]
+        stream_ = torch.cuda.current_stream(device)
+
         def step():
             aaren.aaren_state_init(m, u, st_w)
             for t in range(T):
+                if t % seg == 0:
+                    marks[t // seg].record(stream_)
                 aaren.aaren_step(q, k[t], v[t], m, u, st_w, scale, o_t=o)
+            if T % seg == 0:
+                marks[-1].record(stream_)
+
+        def per_append_by_segment():
+            torch.cuda.synchronize()
+            return [round(marks[i].elapsed_time(marks[i + 1]) * 1e3 / seg, 2)
+                    for i in range(len(marks) - 1)]
+        b.extra = lambda: {"us_per_append_by_eighth": per_append_by_segment()}
         b.step = step
         b.kind = "step"
         b.units = S * H * T
@@ -690,6 +706,7 @@ def main():
         "dtype": b.dtype,
         "data": "synthetic (seeded i.i.d. normal inputs; no dataset)",
         "config": dict(b.config, input_sets=b.sets, input_checksums=checksums,
+                       **(b.extra() if getattr(b, "extra", None) else {}),
                        note=("steps rotate over input copies so that each step reads HBM"
                              if b.sets > 1 else "one input set")),
         "achieved_GBps": achieved,
