@@ -1,0 +1,66 @@
+"""Long look-back chains under repetition: the backward over one stream of
+2^20 rows (8192 tiles, carried from the end), and a packed batch whose one
+long sequence spans thousands of tiles among thousands of short ones. 100
+calls on one workspace must be bitwise identical (the carries are left folds
+in a fixed order whatever the timing) and agree with the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import exact_softmax_attention_02_amd as aaren
+import oracle
+import workloads
+from _gpu import TOL, announce, check, dev, host32, scan_header_error
+
+pytestmark = pytest.mark.gpu
+
+REPEATS = 100
+
+
+def test_backward_one_stream_of_8192_tiles():
+    announce("backward 8192-tile chain x100")
+    B, H, N, d = 1, 1, 1 << 20, 64
+    q, k, v = workloads.dense_inputs(B, H, N, d, seed=15, device=dev())
+    g = torch.randn(B, H, N, d, device=dev(), generator=torch.Generator(device=dev()).manual_seed(16))
+    scale = workloads.default_scale(d)
+    o, lse = aaren.aaren_scan(q, k, v, scale, return_lse=True)
+    ws = torch.zeros(aaren.aaren_scan_backward_workspace_size(B, H, N, d), dtype=torch.uint8,
+                     device=dev())
+    first = [t.clone() for t in aaren.aaren_scan_backward(q, k, v, o, g, lse, scale, workspace=ws)]
+    dq, dk, dv = (torch.empty_like(t) for t in first)
+    for _ in range(REPEATS - 1):
+        aaren.aaren_scan_backward(q, k, v, o, g, lse, scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(dq, first[0]) and torch.equal(dk, first[1]) and torch.equal(dv, first[2])
+    assert scan_header_error(ws) == 0
+    rq, rk, rv = oracle.scan_backward(host32(q), host32(k), host32(v), host32(g), scale)
+    check(first[1], rk, 1e-5, "dk, 8192-tile chain")
+    check(first[2], rv, 1e-5, "dv, 8192-tile chain")
+
+
+def test_packed_long_and_short_sequences():
+    announce("packed long + short sequences x100")
+    rng = np.random.default_rng(17)
+    lengths = np.concatenate([rng.integers(1, 40, size=3000), [1 << 20],
+                              rng.integers(1, 40, size=3000)]).astype(np.int64)
+    H, d = 2, 64
+    q, k, v, offs = workloads.segmented_inputs(lengths, H, d, seed=18, device=dev())
+    T = int(lengths.sum())
+    ws = torch.zeros(aaren.aaren_scan_segmented_workspace_size(len(lengths), T, H, d),
+                     dtype=torch.uint8, device=dev())
+    first = aaren.aaren_scan_segmented(q, k, v, offs, workspace=ws).clone()
+    o = torch.empty_like(first)
+    for _ in range(REPEATS - 1):
+        aaren.aaren_scan_segmented(q, k, v, offs, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, first)
+    assert scan_header_error(ws) == 0
+    # the oracle on the long sequence and on 200 sampled short ones
+    ho = offs.cpu().numpy()
+    scale = workloads.default_scale(d)
+    picks = sorted(set(rng.integers(0, len(lengths), size=200).tolist()) | {3000})
+    for s in picks:
+        a, b = int(ho[s]), int(ho[s + 1])
+        sub = [np.ascontiguousarray(host32(x[a:b]).transpose(1, 0, 2)[None]) for x in (k, v)]
+        ref = oracle.scan(host32(q), sub[0], sub[1], scale)[0].transpose(1, 0, 2)
+        check(first[a:b], ref, TOL[torch.float32], f"sequence {s} of length {b - a}")
