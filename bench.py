@@ -713,6 +713,8 @@ def main():
         "peak_frac": achieved / PEAK_HBM_GBS,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "platform": {"hip": torch.version.hip, "torch": torch.__version__,
+                     "device": torch.cuda.get_device_name(device)},
     }
     print(json.dumps(line), flush=True)
 
