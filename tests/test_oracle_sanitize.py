@@ -1,7 +1,7 @@
 """The C oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
 (gcc, host code) and driven on small and degenerate shapes by
 tests/oracle_sanitize.c: no out-of-bounds access, no undefined behaviour, and
-the driver's value checks hold."""
+the program's own value checks hold."""
 import os
 import shutil
 import subprocess
