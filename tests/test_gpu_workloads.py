@@ -266,3 +266,20 @@ def test_packed_gradients_in_full():
         bound = (per_term[:, None] * np.abs(kh[:, h].astype(np.float64))).sum(axis=0)
         assert np.all(np.abs(host32(dq[h]) - rq[h]) <= bound)
     print(f"packed gradients: T={T} dk {e_k:.3e} dv {e_v:.3e}")
+
+
+def test_mean_query_in_full():
+    """The mean-query workload at full size (B=4, H=8, N=65536, d=128), in the
+    benchmark's call: every (b,h) against the oracle."""
+    w = W["mean_query"]
+    sz = w.sizes
+    B, H, N, d = sz["B"], sz["H"], sz["N"], sz["d"]
+    announce(f"workload mean_query: {w.describe()}")
+    hq, k, v = workloads.mean_query_inputs(B, H, N, d, w.seed, device=dev())
+    scale = workloads.default_scale(d)
+    ws = torch.empty(aaren.aaren_mean_query_attention_workspace_size(B, H, N, d),
+                     dtype=torch.uint8, device=dev())
+    o = aaren.aaren_mean_query_attention(hq, k, v, scale, workspace=ws)
+    ref = oracle.mean_query_attention(host32(hq), host32(k), host32(v), scale)
+    err = check(o, ref, TOL[torch.float32], "mean_query")
+    print(f"mean_query: max scaled err {err:.3e}")
