@@ -15,6 +15,8 @@ from __future__ import annotations
 import torch  # noqa: I001
 
 import ctypes
+import functools
+import itertools
 import math
 import os
 
@@ -86,6 +88,19 @@ def _load():
 
 
 lib = _load()
+
+
+def _on_tensor_device(fn):
+    """Run a binding with its tensors' GPU as the current device: the library
+    launches on the calling thread's current device."""
+    @functools.wraps(fn)
+    def call(*args, **kwargs):
+        for a in itertools.chain(args, kwargs.values()):
+            if isinstance(a, torch.Tensor) and a.is_cuda:
+                with torch.cuda.device(a.device):
+                    return fn(*args, **kwargs)
+        return fn(*args, **kwargs)
+    return call
 
 
 # ---- helpers -----------------------------------------------------------------
@@ -179,6 +194,7 @@ def aaren_reduce_workspace_size(B, H, N, d) -> int:
     return int(lib.aaren_reduce_workspace_size(B, H, N, d))
 
 
+@_on_tensor_device
 def aaren_workspace_clear(workspace: torch.Tensor):
     """Zero a workspace on the current stream (needed once, before first use)."""
     dev = _need_cuda(workspace)
@@ -186,6 +202,7 @@ def aaren_workspace_clear(workspace: torch.Tensor):
                                      _stream(dev)))
 
 
+@_on_tensor_device
 def aaren_scan(q, k, v, scale=None, out_dtype=None, out=None, workspace=None, lse=None,
                return_lse=False):
     """Many-to-many output. q [H,d], k,v [B,H,N,d] -> o [B,H,N,d] (and, with
@@ -211,6 +228,7 @@ def aaren_scan(q, k, v, scale=None, out_dtype=None, out=None, workspace=None, ls
     return (out, lse) if (return_lse or lse is not None) else out
 
 
+@_on_tensor_device
 def aaren_scan_segmented(q, k, v, offsets, scale=None, out_dtype=None, out=None, workspace=None,
                          lse=None, return_lse=False):
     """Each packed sequence scanned on its own. q [H,d], k,v [T,H,d],
@@ -253,6 +271,7 @@ def _backward_dtypes(q, k, v, o, dout, lse):
         raise TypeError("o and lse must be float32 (the forward's float32 outputs)")
 
 
+@_on_tensor_device
 def aaren_scan_backward(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=None,
                         workspace=None):
     """Gradients of the dense many-to-many scan: (dq [H,d], dk, dv [B,H,N,d]),
@@ -278,6 +297,7 @@ def aaren_scan_backward(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=
     return dq, dk, dv
 
 
+@_on_tensor_device
 def aaren_state_init(m, u, w):
     """Write the empty state into m, u [S,H] and w [S,H,d] (float32)."""
     dev = _need_cuda(m, u, w)
@@ -297,6 +317,7 @@ def new_state(S, H, d, device="cuda"):
     return aaren_state_init(m, u, w)
 
 
+@_on_tensor_device
 def aaren_step(q, k_t, v_t, m, u, w, scale=None, out_dtype=None, o_t=None, emit=True):
     """Absorb one pair per (stream, head) into (m, u, w) in place; returns o_t
     [S,H,d] (or None with emit=False)."""
@@ -317,6 +338,7 @@ def aaren_step(q, k_t, v_t, m, u, w, scale=None, out_dtype=None, o_t=None, emit=
     return o_t if emit else None
 
 
+@_on_tensor_device
 def aaren_append(q, k, v, m, u, w, scale=None, out_dtype=None, o=None, emit=True):
     """Append T pairs per (stream, head) to (m, u, w) in place: k, v [T,S,H,d]
     time-major; returns o [T,S,H,d] (or None with emit=False)."""
@@ -339,6 +361,7 @@ def aaren_append(q, k, v, m, u, w, scale=None, out_dtype=None, o=None, emit=True
     return o if emit else None
 
 
+@_on_tensor_device
 def aaren_scan_strided(q, k, v, scale=None, out_dtype=None, out=None, workspace=None, lse=None,
                        return_lse=False):
     """aaren_scan over k, v given as [B,H,N,d] views with any strides whose
@@ -373,6 +396,7 @@ def aaren_layer_workspace_size(B, N, H, d) -> int:
     return int(lib.aaren_layer_workspace_size(B, N, H, d))
 
 
+@_on_tensor_device
 def aaren_layer_forward(x, w_kv, q, scale=None, out_dtype=None, out=None, workspace=None):
     """One Aaren layer: x [B,N,Dm] bf16, w_kv [Dm, 2*H*d] bf16 (W_K | W_V),
     q [H,d] float32 -> o [B,N,H,d] (bf16 by default, so that layers stack)."""
@@ -400,6 +424,7 @@ def aaren_scan_segmented_backward_workspace_size(num_seqs, total_tokens, H, d) -
     return int(lib.aaren_scan_segmented_backward_workspace_size(num_seqs, total_tokens, H, d))
 
 
+@_on_tensor_device
 def aaren_scan_segmented_backward(q, k, v, o, dout, lse, offsets, scale=None, dq=None, dk=None,
                                   dv=None, workspace=None):
     """Gradients of the packed scan: q [H,d]; k, v, dout [T,H,d] (float32 or
@@ -431,6 +456,7 @@ def aaren_mean_query_attention_workspace_size(B, H, N, d) -> int:
     return int(lib.aaren_mean_query_attention_workspace_size(B, H, N, d))
 
 
+@_on_tensor_device
 def aaren_mean_query_attention(hq, k, v, scale=None, out_dtype=None, out=None, g_out=None,
                                return_query=False, workspace=None):
     """Attention of each (b,h)'s mean query over all its pairs: hq, k, v
@@ -458,6 +484,7 @@ def aaren_self_attention_workspace_size(B, H, N, d) -> int:
     return int(lib.aaren_self_attention_workspace_size(B, H, N, d))
 
 
+@_on_tensor_device
 def aaren_self_attention(q, k, v, scale=None, causal=True, out_dtype=None, out=None, lse=None,
                          return_lse=False, workspace=None):
     """Self-attention, one query per token: q, k, v [B,H,N,d] bfloat16 -> o
@@ -481,6 +508,7 @@ def aaren_self_attention(q, k, v, scale=None, causal=True, out_dtype=None, out=N
     return (out, lse) if (return_lse or lse is not None) else out
 
 
+@_on_tensor_device
 def aaren_reduce(q, k, v, scale=None, out_dtype=None, stats=False, out=None, workspace=None):
     """Many-to-one output. q [H,d], k,v [B,H,N,d] -> o [B,H,d] (and, with
     stats, the final state's m and u [B,H] float32)."""

@@ -39,6 +39,8 @@
  *    takes explicit strides); q, k and v share `in_dtype` unless a call says
  *    otherwise; every tensor base pointer must be 16-byte aligned.
  *  - d (head dimension) is 64 or 128.
+ *  - Work runs on the calling thread's current HIP device: tensors,
+ *    workspace and stream must belong to it.
  *  - `hip_stream` is a hipStream_t (NULL = the null stream). Every call only
  *    enqueues work on that stream and returns; device-side faults surface at
  *    the caller's next synchronisation.
