@@ -48,6 +48,12 @@
  *    nothing is enqueued and no output is touched; aaren_last_error() then
  *    holds a description (thread-local).
  *  - Outputs must not alias inputs.
+ *  - HIP graphs: the scans (aaren_scan, aaren_scan_strided,
+ *    aaren_scan_segmented), their gradients and aaren_layer_forward tag the
+ *    states their workgroups exchange with a counter the host advances at
+ *    every call; a graph that captured such a call would replay it with the
+ *    same tag, so these calls must not be captured for replay. The other
+ *    calls enqueue plain kernels only.
  */
 #ifndef AAREN_H
 #define AAREN_H
