@@ -1,0 +1,109 @@
+"""On a rejected call nothing is enqueued and no output changes: each entry
+point is given one invalid argument (through the C ABI, with real device
+buffers) and its outputs, filled beforehand with a sentinel, are compared
+after a synchronisation; the status and aaren_last_error() name the fault."""
+import ctypes
+
+import pytest
+import torch
+
+import exact_softmax_attention_02_amd as aaren
+from _gpu import announce, dev
+
+pytestmark = pytest.mark.gpu
+
+L = aaren.lib
+SENTINEL = 12345.0
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _filled(*shape, dtype=torch.float32):
+    return torch.full(shape, SENTINEL, dtype=dtype, device=dev())
+
+
+def _untouched(*ts):
+    torch.cuda.synchronize()
+    return all(bool((t.float() == SENTINEL).all()) for t in ts)
+
+
+def test_scan_rejections_touch_nothing():
+    announce("errors: scan")
+    B, H, N, d = 2, 3, 500, 64
+    q = torch.randn(H, d, device=dev())
+    k, v = torch.randn(B, H, N, d, device=dev()), torch.randn(B, H, N, d, device=dev())
+    o, lse = _filled(B, H, N, d), _filled(B, H, N)
+    need = aaren.aaren_scan_workspace_size(B, H, N, d)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    call = lambda **kw: L.aaren_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
+                                     kw.get("d", d), 0.125, 0, 0, _ptr(ws), kw.get("wsb", need),
+                                     _stream())
+    assert call(wsb=need - 1) == aaren.AAREN_ERR_WORKSPACE
+    assert "workspace" in aaren.aaren_last_error()
+    assert call(d=96) == aaren.AAREN_ERR_UNSUPPORTED
+    assert _untouched(o, lse)
+    assert call() == aaren.AAREN_OK  # the same call, valid, does write
+    torch.cuda.synchronize()
+    assert not bool((o == SENTINEL).any())
+
+
+def test_backward_and_segmented_rejections_touch_nothing():
+    announce("errors: backward, segmented")
+    B, H, N, d = 1, 2, 300, 64
+    q = torch.randn(H, d, device=dev())
+    k, v, g = (torch.randn(B, H, N, d, device=dev()) for _ in range(3))
+    o, lse = aaren.aaren_scan(q, k, v, return_lse=True)
+    dq, dk, dv = _filled(H, d), _filled(B, H, N, d), _filled(B, H, N, d)
+    need = aaren.aaren_scan_backward_workspace_size(B, H, N, d)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    st = L.aaren_scan_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(g), None, _ptr(dq),
+                               _ptr(dk), _ptr(dv), B, H, N, d, 0.125, 0, _ptr(ws), need, _stream())
+    assert st == aaren.AAREN_ERR_INVALID_ARG  # lse is NULL
+    assert _untouched(dq, dk, dv)
+    # packed: offsets not 8-byte aligned
+    T = 300
+    kp, vp = torch.randn(T, H, d, device=dev()), torch.randn(T, H, d, device=dev())
+    offs = torch.tensor([0, 100, 300, 0], dtype=torch.int64, device=dev())
+    out = _filled(T, H, d)
+    need_s = aaren.aaren_scan_segmented_workspace_size(2, T, H, d)
+    ws_s = torch.zeros(need_s, dtype=torch.uint8, device=dev())
+    bad = ctypes.c_void_p(offs.data_ptr() + 4)
+    st = L.aaren_scan_segmented(_ptr(q), _ptr(kp), _ptr(vp), _ptr(out), None, bad, 2, T, H, d,
+                                0.125, 0, 0, _ptr(ws_s), need_s, _stream())
+    assert st == aaren.AAREN_ERR_ALIGNMENT
+    assert _untouched(out)
+
+
+def test_step_reduce_and_attention_rejections_touch_nothing():
+    announce("errors: step, reduce, self-attention")
+    S, H, d = 64, 2, 64
+    q = torch.randn(H, d, device=dev())
+    kt, vt = torch.randn(S, H, d, device=dev()), torch.randn(S, H, d, device=dev())
+    m, u, w, o = _filled(S, H), _filled(S, H), _filled(S, H, d), _filled(S, H, d)
+    st = L.aaren_step(_ptr(q), _ptr(kt), _ptr(vt), _ptr(m), _ptr(u), _ptr(w), _ptr(o), S, H, d,
+                      0.125, 7, 0, _stream())
+    assert st == aaren.AAREN_ERR_UNSUPPORTED  # unknown input dtype
+    assert _untouched(m, u, w, o)
+    # reduce over N = 0 pairs has no value
+    k0 = torch.empty(1, H, 0, d, device=dev())
+    ro = _filled(1, H, d)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8, device=dev())
+    st = L.aaren_reduce(_ptr(q), _ptr(k0), _ptr(k0), _ptr(ro), None, None, 1, H, 0, d, 0.125,
+                        0, 0, _ptr(ws), 1 << 16, _stream())
+    assert st == aaren.AAREN_ERR_INVALID_ARG
+    assert _untouched(ro)
+    # self-attention takes bf16 only
+    x = torch.randn(1, H, 100, d, device=dev())
+    ao = _filled(1, H, 100, d)
+    need = aaren.aaren_self_attention_workspace_size(1, H, 100, d)
+    wsa = torch.zeros(need, dtype=torch.uint8, device=dev())
+    st = L.aaren_self_attention(_ptr(x), _ptr(x), _ptr(x), _ptr(ao), None, 1, H, 100, d, 0.125,
+                                1, 0, 0, _ptr(wsa), need, _stream())
+    assert st == aaren.AAREN_ERR_UNSUPPORTED
+    assert _untouched(ao)
