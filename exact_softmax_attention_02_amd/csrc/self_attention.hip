@@ -75,8 +75,7 @@ __global__ __launch_bounds__(256) void attn_vmax_kernel(const AttnParams p)
     const uint16_t *src = p.v + (bh * p.N + k0) * D;
     const int64_t chunks = (k1 - k0) * (D / 8);  // 16-byte chunks
     uint32_t mx = 0;
-    for (int64_t c = tid; c < chunks; c += 256) {
-        const u32x4 x = load16(src + 8 * c);
+    auto fold = [&](u32x4 x) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             uint32_t a = x[e] & 0x7fffu, b = (x[e] >> 16) & 0x7fffu;
@@ -85,7 +84,20 @@ __global__ __launch_bounds__(256) void attn_vmax_kernel(const AttnParams p)
             mx = mx > a ? mx : a;
             mx = mx > b ? mx : b;
         }
+    };
+    // four loads in flight per thread, then the remainder
+    int64_t c = tid;
+    for (; c + 3 * 256 < chunks; c += 4 * 256) {
+        u32x4 x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            x[i] = load16(src + 8 * (c + 256 * i));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fold(x[i]);
     }
+    for (; c < chunks; c += 256)
+        fold(load16(src + 8 * c));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const uint32_t o = (uint32_t)__shfl_xor((int)mx, off);
