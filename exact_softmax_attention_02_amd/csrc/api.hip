@@ -35,6 +35,14 @@ bool log_enabled()
     return on;
 }
 
+// Test-only: AAREN_STRESS=1 makes the look-back kernels pause tiles at
+// random (read at every call, so a test can switch it on and off).
+uint32_t stress_enabled()
+{
+    const char *e = std::getenv("AAREN_STRESS");
+    return (e && e[0] && e[0] != '0') ? 1u : 0u;
+}
+
 bool aligned16(const void *p)
 {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
@@ -282,6 +290,7 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
     p.epoch = next_epoch();
+    p.stress = stress_enabled();
     p.qscale = scale * 1.44269504088896340736f;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     p.header = reinterpret_cast<uint32_t *>(ws);
@@ -415,6 +424,7 @@ AAREN_API aaren_status aaren_scan_backward(const void *q, const void *k, const v
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
     p.epoch = next_epoch();
+    p.stress = stress_enabled();
     p.scale = scale;
     p.qscale = scale * 1.44269504088896340736f;
     p.header = reinterpret_cast<uint32_t *>(ws);
@@ -525,6 +535,7 @@ AAREN_API aaren_status aaren_scan_segmented_backward(
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
     p.epoch = next_epoch();
+    p.stress = stress_enabled();
     p.scale = scale;
     p.qscale = scale * 1.44269504088896340736f;
     p.header = reinterpret_cast<uint32_t *>(ws);
@@ -622,6 +633,7 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
     p.epoch = next_epoch();
+    p.stress = stress_enabled();
     p.qscale = scale * 1.44269504088896340736f;
     p.header = reinterpret_cast<uint32_t *>(ws);
     p.counters = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes);

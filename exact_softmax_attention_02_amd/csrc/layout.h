@@ -80,6 +80,7 @@ struct ScanParams {
     uint32_t chunks_padded;  // chunks rounded up to a multiple of group
     uint32_t num_tiles;      // streams * chunks (real tiles)
     uint32_t epoch;          // unique to this call (1 .. 2^31-2)
+    uint32_t stress;         // nonzero: pause tiles at random (tests of the look-back)
     float qscale;            // scale * log2(e)
     uint32_t *header;
     uint32_t *counters;      // [streams * kCounterStride]
@@ -155,6 +156,7 @@ struct BackwardParams {
     uint32_t chunks_padded;
     uint32_t num_tiles;
     uint32_t epoch;
+    uint32_t stress;         // nonzero: pause tiles at random (tests of the look-back)
     float scale;
     float qscale;            // scale * log2(e)
     uint32_t *header;

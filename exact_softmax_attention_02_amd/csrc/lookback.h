@@ -26,6 +26,24 @@ namespace aaren {
 // Aggregates a walk may park before it waits for an inclusive state.
 constexpr int kWindow = 16;
 
+// Scheduling perturbation for tests of the look-back, off in normal use: with
+// `stress` set, a workgroup pauses a pseudo-random 0..7 times 127 x 64 cycles
+// (salt: something that differs between tiles and calls), so that tiles
+// publish and walk in orders the hardware rarely produces by itself. The
+// arguments are wave-uniform.
+__device__ __forceinline__ void stress_pause(uint32_t stress, uint32_t salt)
+{
+    if (stress) {
+        uint32_t h = salt * 0x9e3779b9u;
+        h ^= h >> 15;
+        h *= 0x85ebca6bu;
+        h ^= h >> 13;
+        const int n = (int)(h & 7u);
+        for (int i = 0; i < n; ++i)
+            __builtin_amdgcn_s_sleep(127);
+    }
+}
+
 __device__ __forceinline__ bool tag_ok(uint64_t word, uint32_t epoch)
 {
     return (uint32_t)(word >> 33) == epoch;

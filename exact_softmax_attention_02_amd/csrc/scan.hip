@@ -85,6 +85,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
                                                  p.chunks_padded - 1u, __ATOMIC_RELAXED, "agent");
     __syncthreads();
     const uint32_t chunk32 = __builtin_amdgcn_readfirstlane(sh_chunk);
+    stress_pause(p.stress, blockIdx.x ^ (chunk32 << 12) ^ (p.epoch << 24));
     const uint32_t epoch = p.epoch;
     if (chunk32 >= (uint32_t)p.chunks && chunk32 < p.chunks_padded)
         return;  // a padding position past the end of the stream: nothing to do
@@ -254,6 +255,7 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
                 publish<D>(my, epoch << 1, am, au, aw, lane);
             else
                 publish<D>(my, (epoch << 1) | 1u, am, au, aw, lane);
+            stress_pause(p.stress, blockIdx.x * 3u + epoch);
             // the carry is the left fold A_0 (+) ... (+) A_{j-1} of the stream's
             // earlier aggregates (from its last sequence start, packed batches)
             lookback<D, SEG, false>(p.slots, tile - p.streams, -p.streams, p.num_tiles, epoch,

@@ -109,6 +109,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
                                                  p.chunks_padded - 1u, __ATOMIC_RELAXED, "agent");
     __syncthreads();
     const uint32_t ticket = __builtin_amdgcn_readfirstlane(sh_chunk);
+    stress_pause(p.stress, blockIdx.x ^ (ticket << 12) ^ (p.epoch << 24));
     const uint32_t epoch = p.epoch;
     if (ticket >= (uint32_t)p.chunks && ticket < p.chunks_padded)
         return;  // a padding position: nothing to do
@@ -279,6 +280,7 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
         const bool need_carry = chunk < p.chunks - 1 && !(SEG && sh_last_end);
         if (need_carry) {
             publish<D>(my, (epoch << 1) | (af ? 1u : 0u), am, au, aw, lane);
+            stress_pause(p.stress, blockIdx.x * 3u + epoch);
             // the carry is A_{j+1} (+) ... (+) A_last, the stream's later
             // aggregates (up to the next sequence end, packed batches)
             lookback<D, SEG, true>(p.slots, tile + p.streams, p.streams, p.num_tiles, epoch,

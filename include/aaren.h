@@ -48,6 +48,10 @@
  *    nothing is enqueued and no output is touched; aaren_last_error() then
  *    holds a description (thread-local).
  *  - Outputs must not alias inputs.
+ *  - Environment: AAREN_LOG=1 prints each call's launch geometry to stderr;
+ *    AAREN_STRESS=1 (tests only, read at every call) makes the scans and
+ *    their gradients pause tiles at random to perturb the order in which
+ *    tiles exchange states; results are unchanged, only slower.
  *  - HIP graphs: the scans (aaren_scan, aaren_scan_strided,
  *    aaren_scan_segmented), their gradients and aaren_layer_forward tag the
  *    states their workgroups exchange with a counter the host advances at

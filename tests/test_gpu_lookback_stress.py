@@ -64,3 +64,30 @@ def test_packed_long_and_short_sequences():
         sub = [np.ascontiguousarray(host32(x[a:b]).transpose(1, 0, 2)[None]) for x in (k, v)]
         ref = oracle.scan(host32(q), sub[0], sub[1], scale)[0].transpose(1, 0, 2)
         check(first[a:b], ref, TOL[torch.float32], f"sequence {s} of length {b - a}")
+
+
+def test_perturbed_schedules_give_the_same_bits(monkeypatch):
+    """With AAREN_STRESS=1 every tile pauses a pseudo-random time after taking
+    its ticket and after publishing its aggregate, so tiles publish and walk
+    in unusual orders; the forward, backward and packed results must still be
+    bitwise those of unperturbed calls."""
+    announce("look-back under perturbed schedules")
+    B, H, N, d = 1, 2, 1 << 19, 64
+    q, k, v = workloads.dense_inputs(B, H, N, d, seed=19, device=dev())
+    g = torch.randn(B, H, N, d, device=dev(), generator=torch.Generator(device=dev()).manual_seed(20))
+    o, lse = aaren.aaren_scan(q, k, v, return_lse=True)
+    grads = aaren.aaren_scan_backward(q, k, v, o, g, lse)
+    lengths = np.array([3, 70000, 1, 129, 5000, 2, 100000, 17], np.int64)
+    qp, kp, vp, offs = workloads.segmented_inputs(lengths, H, d, seed=21, device=dev())
+    op = aaren.aaren_scan_segmented(qp, kp, vp, offs)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("AAREN_STRESS", "1")
+    for _ in range(3):
+        o2, lse2 = aaren.aaren_scan(q, k, v, return_lse=True)
+        grads2 = aaren.aaren_scan_backward(q, k, v, o, g, lse)
+        op2 = aaren.aaren_scan_segmented(qp, kp, vp, offs)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o) and torch.equal(lse2, lse)
+        assert all(torch.equal(a, b) for a, b in zip(grads2, grads))
+        assert torch.equal(op2, op)
+    monkeypatch.delenv("AAREN_STRESS")
