@@ -790,6 +790,9 @@ AAREN_API aaren_status aaren_self_attention(const void *q, const void *k, const 
     CHECK(check_common(d, in_dtype, out_dtype));
     if (in_dtype != AAREN_BF16)
         return fail(AAREN_ERR_UNSUPPORTED, "self-attention takes bfloat16 q, k, v");
+    if (N > aaren::kAttnMaxN)
+        return fail(AAREN_ERR_UNSUPPORTED, "self-attention takes N <= %lld (N = %lld)",
+                    (long long)aaren::kAttnMaxN, (long long)N);
     const int64_t elems = mul_checked({B, H, N, d});
     if (elems < 0 || mul_checked({B, H, d, aaren::attn_padded_keys(N)}) < 0)
         return fail(AAREN_ERR_UNSUPPORTED, "B*H*N*d overflows");

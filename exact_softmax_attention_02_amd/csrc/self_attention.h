@@ -16,6 +16,13 @@ namespace aaren {
 constexpr int kAttnWaves = 4;
 constexpr int kAttnQueries = 32 * kAttnWaves;
 constexpr int kAttnKeys = 64;
+// heads whose query tiles are interleaved in the launch order
+constexpr int64_t kAttnHeadGroup = 8;
+
+// Longest sequence: the tile copies address one head's K and transposed V
+// through buffer descriptors whose byte counts and offsets must stay below
+// 2^31 (2^22 keys of 128 bf16 values are 2^30 bytes).
+constexpr int64_t kAttnMaxN = int64_t(1) << 22;
 
 // Rows of the transposed-value workspace are padded to a whole number of key
 // tiles (the padding holds zeros).

@@ -45,8 +45,12 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(1))) void *gptr;
 typedef __attribute__((address_space(3))) void *lptr;
+
+// Fourth word of a raw buffer descriptor on gfx9-family chips (32-bit data
+// format, no stride, no swizzle): buffer loads then read bytes [0, count) of
+// the buffer and return zeros beyond.
+constexpr int kBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, bf16x8 b, f32x16 c)
 {
@@ -193,11 +197,17 @@ __global__ __launch_bounds__(64 * kAttnWaves, 8 / kAttnWaves) void self_attentio
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h32 = lane >> 5, l32 = lane & 31;
-    // workgroups of one head are adjacent (they share its keys in the caches);
-    // within a head the longest causal rows go first
+    // Heads go in groups of kAttnHeadGroup; within a group the query tiles go
+    // longest first (causal), the group's heads taking turns. Workgroups are
+    // dealt to the 8 XCDs in turn, so each XCD serves one head of a group (its
+    // L2 holds that head's keys), and every XCD's own list runs longest first
+    // across its heads, which keeps the causal tail short.
     const int64_t nqt = (p.N + kAttnQueries - 1) / kAttnQueries;
-    const int64_t bh = blockIdx.x / nqt;
-    const int64_t q0 = (nqt - 1 - (int64_t)(blockIdx.x % nqt)) * kAttnQueries;
+    const int64_t g0 = (int64_t)blockIdx.x / (kAttnHeadGroup * nqt) * kAttnHeadGroup;
+    const int64_t gs = p.bh - g0 < kAttnHeadGroup ? p.bh - g0 : kAttnHeadGroup;
+    const int64_t r = (int64_t)blockIdx.x - g0 * nqt;
+    const int64_t bh = g0 + r % gs;
+    const int64_t q0 = (nqt - 1 - r / gs) * kAttnQueries;
     const int64_t qi = q0 + 32 * wave + l32;  // this lane's query
 
     // a negative scale is moved into q (flipping a bf16 sign is exact), so the
@@ -216,36 +226,49 @@ __global__ __launch_bounds__(64 * kAttnWaves, 8 / kAttnWaves) void self_attentio
     const int64_t kend = (p.causal && q0 + kAttnQueries < p.N) ? q0 + kAttnQueries : p.N;
     const int ntiles = (int)((kend + kAttnKeys - 1) / kAttnKeys);
 
-    // Tiles go from global memory straight into LDS (global_load_lds: lane i
-    // of a wave writes 16 bytes at base + 16 i). Rows are unpadded; the
-    // 16-byte chunks of a row are stored XOR-swizzled so that the fragment
-    // reads below (16 lanes, 16 different rows, one chunk column) hit 16
-    // different bank groups: K row r (D/8 chunks) keeps chunk c at position
+    // Tiles go from global memory straight into LDS (buffer loads with the
+    // lds flag: lane i of a wave writes 16 bytes at M0 + 16 i). Rows are
+    // unpadded; the 16-byte chunks of a row are stored XOR-swizzled so that the
+    // fragment reads below (16 lanes, 16 different rows, one chunk column) hit
+    // 16 different bank groups: K row r (D/8 chunks) keeps chunk c at position
     // c ^ kswz(r); a V^T row (8 chunks of 8 keys) at c ^ vswz(r).
     auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
     auto vswz = [](int r) { return (r >> 1) & 7; };
     constexpr int KRPI = 1024 / (2 * D);  // K rows per 1 KB copy
     const uint16_t *kh = p.k + bh * p.N * D;
     const uint16_t *vth = p.vt + bh * D * p.Np;
+    // Copy c of a wave fills 1 KB block kAttnWaves * c + wave of the tile: the
+    // rows of its copy 0 plus 16c (K, d = 128), 32c (K, d = 64) or 32c (V^T).
+    // Both swizzles depend on a row modulo 16 only, so every copy of a lane
+    // uses copy 0's byte offset (one VGPR per operand); the rest is scalar: a
+    // K copy has its own buffer starting c * 4 KB further, whose record count
+    // ends at the head's last key (rows past N read as zeros, masked later),
+    // and a V^T copy adds c * 32 rows as the scalar offset (V^T reads never
+    // leave the head's padded rows). Offsets and counts stay below 2^31 for
+    // N <= kAttnMaxN.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int kr0 = wv * KRPI + lane / (D / 8);
+    const uint32_t koff = (uint32_t)(kr0 * 2 * D + 16 * ((lane % (D / 8)) ^ kswz(kr0)));
+    const int vr0 = wv * 8 + lane / 8;
+    const uint32_t voff = (uint32_t)(vr0 * 2 * p.Np + 16 * ((lane % 8) ^ vswz(vr0)));
+    const uint32_t vstep = (uint32_t)(64 * p.Np);  // 32 V^T rows, in bytes
     auto load_tile = [&](int j, int buf) {
         const int64_t k0 = (int64_t)j * kAttnKeys;
+        const int64_t kbytes = (p.N - k0) * 2 * D;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-            const int blk = kAttnWaves * c + wave;  // 1 KB block of the tile this copy fills
-            const int row = blk * KRPI + lane / (D / 8), pos = lane % (D / 8);
-            int64_t key = k0 + row;
-            key = key < p.N ? key : p.N - 1;  // rows past N: a real row, masked later
-            __builtin_amdgcn_global_load_lds(
-                (gptr)(kh + key * D + 8 * (pos ^ kswz(row))), (lptr)(&sk[buf][blk * 512]), 16, 0, 0);
+            const int64_t left = kbytes - 4096 * c;
+            const auto kr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(kh + k0 * D + 2048 * c), (short)0, (int)(left > 0 ? left : 0), kBufferWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lptr)(&sk[buf][(kAttnWaves * c + wv) * 512]),
+                                                     16, koff, 0, 0, 0);
         }
+        const auto vr = __builtin_amdgcn_make_buffer_rsrc((void *)(vth + k0), (short)0,
+                                                          (int)((D * p.Np - k0) * 2), kBufferWord3);
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            const int blk = kAttnWaves * c + wave;
-            const int row = blk * 8 + lane / 8, pos = lane % 8;
-            __builtin_amdgcn_global_load_lds(
-                (gptr)(vth + row * p.Np + k0 + 8 * (pos ^ vswz(row))), (lptr)(&sv[buf][blk * 512]),
-                16, 0, 0);
-        }
+        for (int c = 0; c < KC; ++c)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lptr)(&sv[buf][(kAttnWaves * c + wv) * 512]),
+                                                     16, voff, vstep * c, 0, 0);
     };
 
     load_tile(0, 0);

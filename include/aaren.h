@@ -302,7 +302,8 @@ aaren_status aaren_layer_forward(const void *x, const void *w_kv, const float *q
  * The workspace (size from the query; no zero-fill needed, every call
  * overwrites what it reads) holds the scaled V transposed and the per-(b,h)
  * magnitude maxima. B*H*N = 0: OK, nothing is read or written. Statuses as
- * for aaren_scan; UNSUPPORTED also for float32 inputs and for B*H > 65535. */
+ * for aaren_scan; UNSUPPORTED also for float32 inputs, for N > 2^22
+ * (4,194,304) and for B*H > 65535. */
 size_t aaren_self_attention_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d);
 aaren_status aaren_self_attention(const void *q, const void *k, const void *v, void *o,
                                   float *lse, int64_t B, int64_t H, int64_t N, int64_t d,

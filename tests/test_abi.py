@@ -142,6 +142,8 @@ def test_self_attention_validation():
     assert sa(inp=0) == S["unsup"]           # float32 inputs: bf16 only
     assert sa(d=96) == S["unsup"]
     assert sa(N=-1) == S["arg"]
+    assert sa(N=(1 << 22) + 1) == S["unsup"]  # tile buffers address at most 2^22 keys
+    assert sa(N=1 << 22) == S["ws"]           # the longest N passes on to the workspace check
     assert sa(o=0) == S["arg"]
     assert sa(o=A + 4) == S["align"]
     assert sa(lse=A + 2) == S["align"]
