@@ -12,7 +12,9 @@
 namespace aaren {
 
 // Tile shapes: a workgroup of kAttnWaves waves takes 32 queries per wave; keys
-// and values go through LDS 64 at a time.
+// and values go through LDS 64 at a time, double buffered (64 KB at d = 128,
+// 32 KB at d = 64). d = 128 runs 2 waves per SIMD (256 VGPRs); d = 64 is held
+// to 128 VGPRs, so four workgroups per CU make 4.
 constexpr int kAttnWaves = 4;
 constexpr int kAttnQueries = 32 * kAttnWaves;
 constexpr int kAttnKeys = 64;

@@ -187,7 +187,7 @@ __device__ __forceinline__ void store4(Tout *dst, float a, float b, float c, flo
 }
 
 template <int D, typename Tout>
-__global__ __launch_bounds__(64 * kAttnWaves, 8 / kAttnWaves) void self_attention_kernel(const AttnParams p)
+__global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attention_kernel(const AttnParams p)
 {
     constexpr int KS = D / 16;          // 16-wide k-steps of S^T = K Q^T
     constexpr int DT = D / 32;          // 32-row tiles of O^T
