@@ -292,15 +292,32 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
     // exactly 0).
     auto tile = [&](int buf, int lim, auto edge_tag) {
         constexpr bool EDGE = decltype(edge_tag)::value;
-        f32x16 s[2];
+        auto kfrag = [&](int t, int kk) {
+            return load16(&sk[buf][(32 * t + krow) * D + 8 * ((2 * kk + h32) ^ kswz(32 * t + krow))]);
+        };
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+        if constexpr (D == 128) {
+            // all 16 K fragments are read before the products (the registers
+            // are free at this point of the tile); read one at a time, each
+            // product of the first chain waited for its own LDS read
+            u32x4 kf[2][KS];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            s[t] = f32x16{};
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk)
+                    kf[t][kk] = kfrag(t, kk);
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk)
-                s[t] = mfma32(load16(&sk[buf][(32 * t + krow) * D +
-                                              8 * ((2 * kk + h32) ^ kswz(32 * t + krow))]),
-                              qf[kk], s[t]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    s[t] = mfma32(kf[t][kk], qf[kk], s[t]);
+        } else {
+            // d = 64 is held to 128 VGPRs: fragments are read at their products
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk)
+                    s[t] = mfma32(kfrag(t, kk), qf[kk], s[t]);
         }
         auto key_off = [&](int t, int r) { return 32 * t + 16 * (r >> 3) + 8 * h32 + (r & 7); };
         float tx = kNegInf;
@@ -309,7 +326,13 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 tx = fmaxf(tx, (!EDGE || key_off(t, r) < lim) ? s[t][r] : kNegInf);
-        tx = fmaxf(tx, __shfl_xor(tx, 32));
+        {
+            // lanes l and l ^ 32 hold the same query: v_permlane32_swap of tx
+            // with itself gives one of them in each result
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tx), __float_as_uint(tx),
+                                                             false, false);
+            tx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
         // The maximum is moved only when a score exceeds it by more than 8
         // (log2 units): the weights then stay below 2^8 (2^15 with the 2^7
         // offset), and the rescale of O (and its register traffic) is skipped
