@@ -106,3 +106,22 @@ def test_value_magnitudes(d):
         err = oracle.max_scaled_err(o / sn, ref / sn)
         assert err <= TOL[torch.bfloat16], (causal, err)
         print(f"value magnitudes d={d} causal={causal}: o/s {err:.2e}")
+
+
+def test_longest_sequence():
+    """N = 2^22, the longest the entry point takes, at d = 128: the tile
+    copies' buffer byte counts reach 2^30 there. Sampled rows at the start,
+    the middle and the end (the last rows read every key of the head)."""
+    B, H, N, d = 1, 1, 1 << 22, 128
+    announce(f"self-attention longest sequence B={B} H={H} N={N} d={d} causal")
+    q, k, v = inputs(B, H, N, d, seed=23)
+    scale = float(np.float32(d ** -0.5))
+    o, lse = aaren.aaren_self_attention(q, k, v, scale, return_lse=True)
+    torch.cuda.synchronize()
+    qh, kh, vh = host32(q), host32(k), host32(v)
+    worst = 0.0
+    for a, b in ((0, 8), (N // 2 - 4, N // 2 + 4), (N - 8, N)):
+        ref, rl = oracle.self_attention(qh, kh, vh, scale, causal=True, rows=(a, b), stats=True)
+        worst = max(worst, check(o[:, :, a:b], ref, TOL[torch.bfloat16], f"rows {a}..{b}"))
+        assert oracle.max_scaled_err(host32(lse[:, :, a:b]), rl) <= 1e-5
+    print(f"self-attention N=2^22: max scaled err over 24 rows {worst:.3e}")
