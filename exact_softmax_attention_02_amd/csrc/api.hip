@@ -113,11 +113,31 @@ size_t scan_workspace_bytes(int64_t streams, int64_t tiles, int64_t bitmap_words
 }
 
 // Each scan call tags what it publishes with an epoch no other call of this
-// process uses (1 .. 2^31-2, wrapping after 2^31-2 calls).
+// process uses: eager calls 1 .. kGraphEpoch0 - 1 from this counter (wrapping
+// after 2^30 - 1 calls); calls captured into a HIP graph a device-side epoch
+// (see kEpochWord), marked here by 0.
 uint32_t next_epoch()
 {
     static std::atomic<uint32_t> counter{0};
-    return counter.fetch_add(1, std::memory_order_relaxed) % 0x7ffffffeu + 1u;
+    return counter.fetch_add(1, std::memory_order_relaxed) % (aaren::kGraphEpoch0 - 1u) + 1u;
+}
+
+bool capturing(hipStream_t stream)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &st) == hipSuccess && st == hipStreamCaptureStatusActive;
+}
+
+// The call's epoch: the host's next one, or (under graph capture) 0 after
+// enqueueing the device-side advance of the header's epoch word.
+aaren_status call_epoch(uint32_t *header, hipStream_t stream, uint32_t *epoch)
+{
+    if (!capturing(stream)) {
+        *epoch = next_epoch();
+        return AAREN_OK;
+    }
+    *epoch = 0;
+    return hip_status(aaren::launch_epoch_advance(header, stream), "epoch advance launch");
 }
 
 int64_t ceil_div(int64_t a, int64_t b)
@@ -289,7 +309,6 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
     p.group = group;
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
-    p.epoch = next_epoch();
     p.stress = stress_enabled();
     p.qscale = scale * 1.44269504088896340736f;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -301,6 +320,7 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
                 (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles, rows);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     CHECK(prepare_counters(workspace, counter_bytes(B * H), st));
+    CHECK(call_epoch(p.header, st, &p.epoch));
     return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, false, st),
                       "scan launch");
 }
@@ -423,7 +443,6 @@ AAREN_API aaren_status aaren_scan_backward(const void *q, const void *k, const v
     p.group = kGroupDense;
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
-    p.epoch = next_epoch();
     p.stress = stress_enabled();
     p.scale = scale;
     p.qscale = scale * 1.44269504088896340736f;
@@ -436,6 +455,7 @@ AAREN_API aaren_status aaren_scan_backward(const void *q, const void *k, const v
         fprintf(stderr, "[aaren] scan_backward B=%lld H=%lld N=%lld d=%lld tiles=%lld\n",
                 (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles);
     CHECK(prepare_counters(workspace, counter_bytes(B * H), st));
+    CHECK(call_epoch(p.header, st, &p.epoch));
     return hip_status(aaren::launch_scan_backward(p, (int)d, false, in_dtype, st),
                       "scan backward launch");
 }
@@ -534,7 +554,6 @@ AAREN_API aaren_status aaren_scan_segmented_backward(
     p.group = kGroupPacked;
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
-    p.epoch = next_epoch();
     p.stress = stress_enabled();
     p.scale = scale;
     p.qscale = scale * 1.44269504088896340736f;
@@ -548,6 +567,7 @@ AAREN_API aaren_status aaren_scan_segmented_backward(
         fprintf(stderr, "[aaren] scan_segmented_backward S=%lld T=%lld H=%lld d=%lld tiles=%lld\n",
                 (long long)num_seqs, (long long)T, (long long)H, (long long)d, (long long)tiles);
     CHECK(prepare_counters(workspace, counter_bytes(H), st));
+    CHECK(call_epoch(p.header, st, &p.epoch));
     CHECK(hip_status(aaren::launch_segment_flags(offsets, num_seqs, T, bitmap, words, st),
                      "segment flags launch"));
     return hip_status(aaren::launch_scan_backward(p, (int)d, true, in_dtype, st),
@@ -632,7 +652,6 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
     p.group = kGroupPacked;
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
-    p.epoch = next_epoch();
     p.stress = stress_enabled();
     p.qscale = scale * 1.44269504088896340736f;
     p.header = reinterpret_cast<uint32_t *>(ws);
@@ -645,6 +664,7 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
                 (long long)num_seqs, (long long)total_tokens, (long long)H, (long long)d,
                 (long long)tiles);
     CHECK(prepare_counters(workspace, counter_bytes(H), st));
+    CHECK(call_epoch(p.header, st, &p.epoch));
     CHECK(hip_status(aaren::launch_segment_flags(offsets, num_seqs, total_tokens, bitmap, words, st),
                      "segment flag launch"));
     return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, true, st),

@@ -28,6 +28,16 @@ namespace aaren {
 //   the slots never need resetting. flag marks an aggregate that contains a
 //   sequence start.
 constexpr int kError = 3;
+// header[kEpochWord]: the epoch of the last call made while its stream was
+// being captured into a HIP graph. Eager calls take their epoch from a
+// process-wide counter on the host (1 .. kGraphEpoch0 - 1) and pass it to the
+// kernels; a captured call instead enqueues a one-thread kernel that advances
+// this word (kGraphEpoch0 .. kGraphEpochEnd - 1, wrapping), and its kernels,
+// given epoch 0, read the word: every replay of the graph then runs with an
+// epoch of its own, and the two ranges never meet.
+constexpr int kEpochWord = 4;
+constexpr uint32_t kGraphEpoch0 = 1u << 30;
+constexpr uint32_t kGraphEpochEnd = 0x7fffffffu;
 constexpr size_t kHeaderBytes = 256;
 constexpr int kCounterStride = 32;  // u32 words between ticket counters (128 B)
 // polls of a predecessor's slots before a tile gives up (about a second)
@@ -79,7 +89,7 @@ struct ScanParams {
     uint32_t group;          // consecutive workgroups that serve one stream
     uint32_t chunks_padded;  // chunks rounded up to a multiple of group
     uint32_t num_tiles;      // streams * chunks (real tiles)
-    uint32_t epoch;          // unique to this call (1 .. 2^31-2)
+    uint32_t epoch;          // unique to this call; 0: read header[kEpochWord]
     uint32_t stress;         // nonzero: pause tiles at random (tests of the look-back)
     float qscale;            // scale * log2(e)
     uint32_t *header;
@@ -177,6 +187,7 @@ hipError_t launch_append(const StepParams &p, int D, aaren_dtype in, aaren_dtype
 hipError_t launch_state_init(float *m, float *u, float *w, int64_t units, int64_t D,
                              hipStream_t stream);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
+hipError_t launch_epoch_advance(uint32_t *header, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams &p, int D, aaren_dtype in, aaren_dtype out,
                          hipStream_t stream);
 int reduce_rows_per_iteration(int D, aaren_dtype in);

@@ -85,8 +85,13 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
                                                  p.chunks_padded - 1u, __ATOMIC_RELAXED, "agent");
     __syncthreads();
     const uint32_t chunk32 = __builtin_amdgcn_readfirstlane(sh_chunk);
-    stress_pause(p.stress, blockIdx.x ^ (chunk32 << 12) ^ (p.epoch << 24));
-    const uint32_t epoch = p.epoch;
+    // a call captured into a graph finds its epoch in the header (advanced
+    // on the device just before this launch)
+    const uint32_t epoch =
+        p.epoch ? p.epoch
+                : __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                      p.header + kEpochWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    stress_pause(p.stress, blockIdx.x ^ (chunk32 << 12) ^ (epoch << 24));
     if (chunk32 >= (uint32_t)p.chunks && chunk32 < p.chunks_padded)
         return;  // a padding position past the end of the stream: nothing to do
     if (chunk32 >= (uint32_t)p.chunks) {  // counter not at zero: refuse to run

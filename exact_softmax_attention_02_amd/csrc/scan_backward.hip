@@ -109,8 +109,13 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
                                                  p.chunks_padded - 1u, __ATOMIC_RELAXED, "agent");
     __syncthreads();
     const uint32_t ticket = __builtin_amdgcn_readfirstlane(sh_chunk);
-    stress_pause(p.stress, blockIdx.x ^ (ticket << 12) ^ (p.epoch << 24));
-    const uint32_t epoch = p.epoch;
+    // a call captured into a graph finds its epoch in the header (advanced
+    // on the device just before this launch)
+    const uint32_t epoch =
+        p.epoch ? p.epoch
+                : __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                      p.header + kEpochWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    stress_pause(p.stress, blockIdx.x ^ (ticket << 12) ^ (epoch << 24));
     if (ticket >= (uint32_t)p.chunks && ticket < p.chunks_padded)
         return;  // a padding position: nothing to do
     if (ticket >= (uint32_t)p.chunks) {

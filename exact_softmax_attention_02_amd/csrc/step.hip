@@ -274,6 +274,21 @@ hipError_t launch_state_init(float *m, float *u, float *w, int64_t units, int64_
     return hipGetLastError();
 }
 
+// The next graph epoch in the workspace header (see kEpochWord).
+__global__ __launch_bounds__(64) void epoch_advance_kernel(uint32_t *header)
+{
+    if (threadIdx.x == 0) {
+        const uint32_t e = header[kEpochWord];
+        header[kEpochWord] = (e < kGraphEpoch0 || e + 1 >= kGraphEpochEnd) ? kGraphEpoch0 : e + 1;
+    }
+}
+
+hipError_t launch_epoch_advance(uint32_t *header, hipStream_t stream)
+{
+    hipLaunchKernelGGL(epoch_advance_kernel, dim3(1), dim3(64), 0, stream, header);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream)
 {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for((int64_t)(bytes / 16) + 1)), dim3(256), 0,

@@ -52,12 +52,18 @@
  *    AAREN_STRESS=1 (tests only, read at every call) makes the scans and
  *    their gradients pause tiles at random to perturb the order in which
  *    tiles exchange states; results are unchanged, only slower.
- *  - HIP graphs: the scans (aaren_scan, aaren_scan_strided,
- *    aaren_scan_segmented), their gradients and aaren_layer_forward tag the
- *    states their workgroups exchange with a counter the host advances at
- *    every call; a graph that captured such a call would replay it with the
- *    same tag, so these calls must not be captured for replay. The other
- *    calls enqueue plain kernels only.
+ *  - HIP graphs: every call may be captured for replay, except
+ *    aaren_layer_forward (its rocBLAS product is not checked under capture).
+ *    The scans (aaren_scan, aaren_scan_strided, aaren_scan_segmented) and
+ *    their gradients tag the states their workgroups exchange with an epoch:
+ *    an eager call takes it from a counter on the host; a call made while its
+ *    stream is being captured (hipStreamIsCapturing) enqueues one more
+ *    one-thread kernel that advances an epoch word in the workspace header,
+ *    which the call's kernels then read, so every replay runs with an epoch
+ *    of its own. Eager and captured calls may share a workspace (the two
+ *    kinds of epoch are drawn from disjoint ranges), but replays and calls
+ *    on one workspace must not overlap in time, like any two calls on it.
+ *    No call enqueues a memset.
  */
 #ifndef AAREN_H
 #define AAREN_H

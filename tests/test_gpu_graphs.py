@@ -1,14 +1,20 @@
-"""The calls that launch plain kernels (no look-back epoch, no memset) under
-HIP graph capture: self-attention, the reduction and the step, each captured
-once and replayed several times with the program's own eager work and
-synchronisations between replays; every replay must equal the eager result
-bit for bit."""
+"""Calls under HIP graph capture, each captured once and replayed several
+times with the program's own eager work and synchronisations between
+replays; every replay must equal the eager result bit for bit.
+
+Self-attention, the reduction and the step launch plain kernels. The scans
+and their gradients exchange states between tiles tagged with an epoch:
+captured, they advance an epoch word in the workspace on the device before
+each launch, so replays on new inputs (copied into the captured tensors) are
+checked against eager calls on those inputs, made on the same workspace in
+between (eager calls use host epochs, which never meet the graph's)."""
+import numpy as np
 import pytest
 import torch
 
 import exact_softmax_attention_02_amd as aaren
 import workloads
-from _gpu import announce, dev
+from _gpu import announce, dev, scan_header_error
 
 pytestmark = pytest.mark.gpu
 
@@ -91,3 +97,96 @@ def test_steps_in_a_graph():
         torch.cuda.synchronize()
     assert torch.equal(m2, ref[0]) and torch.equal(u2, ref[1]) and torch.equal(w2, ref[2])
     assert torch.equal(o, ref[3])
+
+
+def _refill(gen, *ts):
+    """New values in captured input tensors (same storage)."""
+    for t in ts:
+        t.copy_(torch.randn(t.shape, generator=gen, device=dev()).to(t.dtype))
+
+
+def test_dense_scan_in_a_graph():
+    announce("graph: dense scan")
+    B, H, N, d = 2, 3, 3000, 64            # several tiles per stream
+    g = torch.Generator(device=dev()).manual_seed(31)
+    q, k, v = (torch.empty(*shape, device=dev()) for shape in ((H, d), (B, H, N, d), (B, H, N, d)))
+    _refill(g, q, k, v)
+    ws = torch.zeros(aaren.aaren_scan_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev())
+    o, lse = torch.empty(B, H, N, d, device=dev()), torch.empty(B, H, N, device=dev())
+    aaren.aaren_scan(q, k, v, out=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        aaren.aaren_scan(q, k, v, out=o, lse=lse, workspace=ws)
+    for _ in range(REPLAYS):
+        _refill(g, q, k, v)
+        o.zero_()
+        _noise()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref, ref_l = aaren.aaren_scan(q, k, v, workspace=ws, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref) and torch.equal(lse, ref_l)
+        assert scan_header_error(ws) == 0
+
+
+def test_packed_scan_in_a_graph():
+    announce("graph: packed scan")
+    H, d = 2, 128
+    lengths = [1, 700, 0, 2500, 33]
+    offsets = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int64, device=dev())
+    T = sum(lengths)
+    g = torch.Generator(device=dev()).manual_seed(32)
+    q = torch.empty(H, d, device=dev())
+    k, v = (torch.empty(T, H, d, device=dev(), dtype=torch.bfloat16) for _ in range(2))
+    _refill(g, q, k, v)
+    q = q.to(torch.bfloat16)
+    ws = torch.zeros(aaren.aaren_scan_segmented_workspace_size(len(lengths), T, H, d),
+                     dtype=torch.uint8, device=dev())
+    o = torch.empty(T, H, d, device=dev())
+    aaren.aaren_scan_segmented(q, k, v, offsets, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        aaren.aaren_scan_segmented(q, k, v, offsets, out=o, workspace=ws)
+    for _ in range(REPLAYS):
+        _refill(g, k, v)
+        o.zero_()
+        _noise()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = aaren.aaren_scan_segmented(q, k, v, offsets, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref)
+        assert scan_header_error(ws) == 0
+
+
+def test_scan_gradients_in_a_graph():
+    announce("graph: dense scan gradients")
+    B, H, N, d = 2, 2, 2000, 64
+    g = torch.Generator(device=dev()).manual_seed(33)
+    q, k, v, dout = (torch.empty(*shape, device=dev())
+                     for shape in ((H, d), (B, H, N, d), (B, H, N, d), (B, H, N, d)))
+    _refill(g, q, k, v, dout)
+    o, lse = aaren.aaren_scan(q, k, v, return_lse=True)
+    wsb = torch.zeros(aaren.aaren_scan_backward_workspace_size(B, H, N, d), dtype=torch.uint8,
+                      device=dev())
+    dq, dk, dv = torch.empty(H, d, device=dev()), torch.empty_like(k), torch.empty_like(v)
+    aaren.aaren_scan_backward(q, k, v, o, dout, lse, dq=dq, dk=dk, dv=dv, workspace=wsb)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        aaren.aaren_scan_backward(q, k, v, o, dout, lse, dq=dq, dk=dk, dv=dv, workspace=wsb)
+    for _ in range(REPLAYS):
+        _refill(g, q, k, v, dout)
+        o2, lse2 = aaren.aaren_scan(q, k, v, return_lse=True)   # the forward of the new inputs
+        o.copy_(o2)
+        lse.copy_(lse2)
+        dk.zero_()
+        _noise()
+        graph.replay()
+        torch.cuda.synchronize()
+        rq, rk, rv = aaren.aaren_scan_backward(q, k, v, o, dout, lse, workspace=wsb)
+        torch.cuda.synchronize()
+        assert torch.equal(dq, rq) and torch.equal(dk, rk) and torch.equal(dv, rv)
+        assert scan_header_error(wsb) == 0
