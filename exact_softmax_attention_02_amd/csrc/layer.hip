@@ -99,6 +99,16 @@ AAREN_API aaren_status aaren_layer_forward(const void *x, const void *w_kv, cons
         if (hipGetDevice(&device) != hipSuccess)
             return aaren_layer_fail(AAREN_ERR_HIP, "hipGetDevice failed");
         std::lock_guard<std::mutex> lock(g_blas_mutex);
+        // a handle allocates device memory when it is created, which a stream
+        // being captured into a graph does not allow: the first call on a
+        // device must be an eager one
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (g_blas.find(device) == g_blas.end() &&
+            hipStreamIsCapturing(static_cast<hipStream_t>(hip_stream), &cap) == hipSuccess &&
+            cap == hipStreamCaptureStatusActive)
+            return aaren_layer_fail(AAREN_ERR_UNSUPPORTED,
+                                    "the first layer call on a device cannot be captured into a "
+                                    "graph (it creates the rocBLAS handle); call it once eagerly");
         rocblas_handle h = blas_handle(device);
         if (!h)
             return aaren_layer_fail(AAREN_ERR_HIP, "rocblas_create_handle failed");

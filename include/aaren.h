@@ -52,8 +52,10 @@
  *    AAREN_STRESS=1 (tests only, read at every call) makes the scans and
  *    their gradients pause tiles at random to perturb the order in which
  *    tiles exchange states; results are unchanged, only slower.
- *  - HIP graphs: every call may be captured for replay, except
- *    aaren_layer_forward (its rocBLAS product is not checked under capture).
+ *  - HIP graphs: every call may be captured for replay; aaren_layer_forward
+ *    only after one eager call on the device (its first call creates the
+ *    rocBLAS handle, which allocates; captured first, it returns
+ *    UNSUPPORTED and enqueues nothing).
  *    The scans (aaren_scan, aaren_scan_strided, aaren_scan_segmented) and
  *    their gradients tag the states their workgroups exchange with an epoch:
  *    an eager call takes it from a counter on the host; a call made while its

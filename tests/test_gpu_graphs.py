@@ -8,6 +8,10 @@ captured, they advance an epoch word in the workspace on the device before
 each launch, so replays on new inputs (copied into the captured tensors) are
 checked against eager calls on those inputs, made on the same workspace in
 between (eager calls use host epochs, which never meet the graph's)."""
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -15,6 +19,8 @@ import torch
 import exact_softmax_attention_02_amd as aaren
 import workloads
 from _gpu import announce, dev, scan_header_error
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 pytestmark = pytest.mark.gpu
 
@@ -190,3 +196,63 @@ def test_scan_gradients_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(dq, rq) and torch.equal(dk, rk) and torch.equal(dv, rv)
         assert scan_header_error(wsb) == 0
+
+
+def test_layer_in_a_graph():
+    """The layer (rocBLAS product, then the strided scan) captured after one
+    eager call on the device, replayed on new x."""
+    announce("graph: layer")
+    B, N, Dm, H, d = 2, 1500, 256, 4, 64
+    x, w, q = workloads.layer_inputs(B, N, Dm, H, d, 1, 41, device=dev())
+    w, q = w[0], q[0]
+    wsp = torch.zeros(aaren.aaren_layer_workspace_size(B, N, H, d), dtype=torch.uint8, device=dev())
+    o = torch.empty(B, N, H, d, dtype=torch.bfloat16, device=dev())
+    aaren.aaren_layer_forward(x, w, q, out=o, workspace=wsp)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        aaren.aaren_layer_forward(x, w, q, out=o, workspace=wsp)
+    g = torch.Generator(device=dev()).manual_seed(42)
+    for _ in range(REPLAYS):
+        _refill(g, x)
+        o.zero_()
+        _noise()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = aaren.aaren_layer_forward(x, w, q, workspace=wsp)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref)
+
+
+_FIRST_CAPTURED = """
+import torch, exact_softmax_attention_02_amd as aaren, workloads
+dev = torch.device("cuda:0")
+x, w, q = workloads.layer_inputs(1, 300, 128, 2, 64, 1, 43, device=dev)
+wsp = torch.zeros(aaren.aaren_layer_workspace_size(1, 300, 2, 64), dtype=torch.uint8, device=dev)
+o = torch.empty(1, 300, 2, 64, dtype=torch.bfloat16, device=dev)
+graph = torch.cuda.CUDAGraph()
+try:
+    with torch.cuda.graph(graph):
+        aaren.aaren_layer_forward(x, w[0], q[0], out=o, workspace=wsp)
+    print("captured")
+except aaren.AarenError as e:
+    assert e.status == aaren.AAREN_ERR_UNSUPPORTED, e.status
+    print("refused:", e)
+aaren.aaren_layer_forward(x, w[0], q[0], out=o, workspace=wsp)   # eager calls still work
+torch.cuda.synchronize()
+print("eager after refusal ok")
+"""
+
+
+def test_layer_first_call_captured_is_refused():
+    """In a process whose first layer call is made under capture the call is
+    refused with UNSUPPORTED (creating the rocBLAS handle allocates), enqueues
+    nothing, and later eager calls work. Run in a child process so that no
+    earlier layer call of the test session has created the handle."""
+    announce("graph: layer first call under capture (child process)")
+    env = dict(os.environ, PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CAPTURED], capture_output=True, text=True,
+                       env=env, timeout=120, cwd=ROOT)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "refused:" in r.stdout and "cannot be captured" in r.stdout, r.stdout
+    assert "eager after refusal ok" in r.stdout
