@@ -48,6 +48,12 @@
  *    nothing is enqueued and no output is touched; aaren_last_error() then
  *    holds a description (thread-local).
  *  - Outputs must not alias inputs.
+ *  - Thread safety: any number of host threads may call at once, on the
+ *    same or different devices and streams, provided calls that can run at
+ *    the same time (on different streams) use different workspaces and
+ *    outputs. Library state shared between calls (the epoch counter, the
+ *    record of cleared workspace bytes, the layer's rocBLAS handles) is
+ *    guarded.
  *  - Environment: AAREN_LOG=1 prints each call's launch geometry to stderr;
  *    AAREN_STRESS=1 (tests only, read at every call) makes the scans and
  *    their gradients pause tiles at random to perturb the order in which
