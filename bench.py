@@ -35,7 +35,9 @@ counter file under profiles/ only while the kernel sources still hash to the
 value recorded there; otherwise null.
 
 cpu_baseline times the float64 CPU oracle (as it is, untuned) on the host's
-cores over a bounded sample of the same workload.
+cores over a bounded sample of the same workload; for the dense workload it
+adds the same oracle on one thread (cpu_baseline.one_thread); the single
+sequence is one unit and runs on one thread anyway.
 """
 from __future__ import annotations
 
@@ -685,12 +687,20 @@ def main():
         import oracle
         rate, sample = b.cpu(args.cpu_seconds)
         cores = oracle.threads()
-        if args.workload in ("reduce", "mean_query"):
+        if args.workload in ("reduce", "mean_query", "single"):
             cores = 1  # one unit: the recurrence runs on one thread
         elif args.workload == "ragged_backward":
             cores = min(cores, b.config["H"])  # each sequence's heads are its parallel units
         cpu = {"value": rate, "unit": b.unit, "cores": cores, "kind": "oracle", "sample": sample,
                "cpu_model": host_cpu(), "host_threads": os.cpu_count()}
+        if args.workload == "dense":
+            # the same oracle on one thread, for the single-core rate
+            oracle.set_threads(1)
+            try:
+                rate1, sample1 = b.cpu(max(args.cpu_seconds / 2, 1.0))
+            finally:
+                oracle.set_threads(cores)
+            cpu["one_thread"] = {"value": rate1, "unit": b.unit, "sample": sample1}
 
     line = {
         "metric": "tokens/s and achieved HBM GB/s (% of peak) for aaren_scan at B*H*N, d=64/128"

@@ -48,6 +48,8 @@ def _configure(lib):
     opt64 = ctypes.c_void_p
     i64 = ctypes.c_int64
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_scan.argtypes = [f32p, f32p, f32p, i64, i64, i64, i64, ctypes.c_double,
                                 f64p, opt64, opt64]
     lib.oracle_scan_segmented.argtypes = [f32p, f32p, f32p, i64p, i64, i64, i64, i64,
@@ -87,6 +89,11 @@ def _ptr(a):
 def threads() -> int:
     """OpenMP threads the oracle runs with."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for the loops over independent units (timing only)."""
+    _load().oracle_set_threads(int(n))
 
 
 def scan(q, k, v, scale, stats: bool = False):

@@ -110,6 +110,18 @@ int oracle_threads(void)
 #endif
 }
 
+/* Set the number of threads the loops over independent units use (timing
+   only: every unit is computed the same way whatever the count). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Many-to-many scan over a dense batch.
  * q [H,d]; k, v [B,H,N,d]; o [B,H,N,d]; m_out, lse_out [B,H,N] or NULL. */
 int oracle_scan(const float *q, const float *k, const float *v,
