@@ -645,7 +645,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path is data-parallel over independent "
-              "sequences and this build runs on a single MI355X; --gpus must be 1.",
+              "sequences, and a run of several GPUs would repeat the same per-GPU work; "
+              "--gpus must be 1.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -50,8 +50,8 @@ class AarenError(RuntimeError):
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is not built: run __graft_entry__.build() "
-                          "or python exact_softmax_attention_02_amd/build.py")
+        raise ImportError(f"{_LIB_PATH} is not built: run "
+                          "python exact_softmax_attention_02_amd/build.py")
     lib = ctypes.CDLL(_LIB_PATH)
     P, I64, F, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_int
     sig = {
