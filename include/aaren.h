@@ -109,7 +109,8 @@ const char *aaren_last_error(void);
 /* ---- workspaces ------------------------------------------------------------
  * The scans carry the running state across tiles of a sequence through a
  * caller-owned workspace (per-stream ticket counters and per-tile published
- * states, tagged with a per-call epoch).
+ * states, tagged with a per-call epoch; its header also keeps the epoch of
+ * the calls captured into HIP graphs).
  * Contract:
  *  - size it with the matching *_workspace_size query;
  *  - zero it ONCE before its first use (aaren_workspace_clear does that on a
