@@ -19,7 +19,7 @@ constexpr int kAttnWaves = 4;
 constexpr int kAttnQueries = 32 * kAttnWaves;
 constexpr int kAttnKeys = 64;
 // heads whose query tiles are interleaved in the launch order
-constexpr int64_t kAttnHeadGroup = 8;
+constexpr int64_t kAttnHeadGroup = 16;
 
 // Longest sequence: the tile copies address one head's K and transposed V
 // through buffer descriptors whose byte counts and offsets must stay below

@@ -197,11 +197,11 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h32 = lane >> 5, l32 = lane & 31;
-    // Heads go in groups of kAttnHeadGroup; within a group the query tiles go
-    // longest first (causal), the group's heads taking turns. Workgroups are
-    // dealt to the 8 XCDs in turn, so each XCD serves one head of a group (its
-    // L2 holds that head's keys), and every XCD's own list runs longest first
-    // across its heads, which keeps the causal tail short.
+    // Heads go in groups of kAttnHeadGroup (16); within a group the query
+    // tiles go longest first (causal), the group's heads taking turns.
+    // Workgroups are dealt to the 8 XCDs in turn, so each XCD serves two heads
+    // of a group (its L2 holds their keys), and every XCD's own list runs
+    // longest first across its heads, which keeps the causal tail short.
     const int64_t nqt = (p.N + kAttnQueries - 1) / kAttnQueries;
     const int64_t g0 = (int64_t)blockIdx.x / (kAttnHeadGroup * nqt) * kAttnHeadGroup;
     const int64_t gs = p.bh - g0 < kAttnHeadGroup ? p.bh - g0 : kAttnHeadGroup;
