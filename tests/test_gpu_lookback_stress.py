@@ -91,3 +91,28 @@ def test_perturbed_schedules_give_the_same_bits(monkeypatch):
         assert all(torch.equal(a, b) for a, b in zip(grads2, grads))
         assert torch.equal(op2, op)
     monkeypatch.delenv("AAREN_STRESS")
+
+
+def test_graph_replays_under_perturbed_schedules(monkeypatch):
+    """A dense scan captured into a graph with AAREN_STRESS=1 (tiles pause at
+    random; the calls take device-side epochs) and replayed ten times: every
+    replay equals the unperturbed eager result bit for bit."""
+    announce("graph replays under perturbed schedules")
+    B, H, N, d = 2, 4, 1 << 17, 64
+    q, k, v = workloads.dense_inputs(B, H, N, d, seed=34, device=dev())
+    ref = aaren.aaren_scan(q, k, v)
+    ws = torch.zeros(aaren.aaren_scan_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev())
+    out = torch.empty_like(ref)
+    aaren.aaren_scan(q, k, v, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("AAREN_STRESS", "1")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        aaren.aaren_scan(q, k, v, out=out, workspace=ws)
+    monkeypatch.delenv("AAREN_STRESS")
+    for _ in range(10):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+    assert scan_header_error(ws) == 0
