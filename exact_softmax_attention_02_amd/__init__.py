@@ -7,6 +7,10 @@ include/aaren.h; see there for the definitions and the contract.
 
 There is no fallback: if libaaren.so is missing, importing this package
 fails.
+
+With AAREN_DEBUG=1 in the environment, every scan and scan gradient call
+synchronises afterwards and raises AarenError if its workspace reports that
+a workgroup could not take part normally (see aaren_workspace_status).
 """
 from __future__ import annotations
 
@@ -30,6 +34,7 @@ AAREN_F32, AAREN_BF16 = 0, 1
 
 EXPORTS = (
     "aaren_version", "aaren_status_string", "aaren_last_error", "aaren_workspace_clear",
+    "aaren_init", "aaren_workspace_status", "aaren_scan_lse", "aaren_scan_segmented_lse",
     "aaren_scan_workspace_size", "aaren_scan", "aaren_scan_segmented_workspace_size",
     "aaren_scan_segmented", "aaren_state_init", "aaren_step", "aaren_reduce_workspace_size",
     "aaren_reduce", "aaren_scan_backward_workspace_size", "aaren_scan_backward", "aaren_append",
@@ -59,10 +64,15 @@ def _load():
         "aaren_status_string": (ctypes.c_char_p, [I]),
         "aaren_last_error": (ctypes.c_char_p, []),
         "aaren_workspace_clear": (I, [P, SZ, P]),
+        "aaren_init": (I, []),
+        "aaren_workspace_status": (I, [P, SZ, P, I, P]),
         "aaren_scan_workspace_size": (SZ, [I64, I64, I64, I64]),
-        "aaren_scan": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
+        "aaren_scan": (I, [P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
+        "aaren_scan_lse": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
         "aaren_scan_segmented_workspace_size": (SZ, [I64, I64, I64, I64]),
-        "aaren_scan_segmented": (I, [P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
+        "aaren_scan_segmented": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
+        "aaren_scan_segmented_lse": (I, [P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ,
+                                         P]),
         "aaren_state_init": (I, [P, P, P, I64, I64, I64, P]),
         "aaren_step": (I, [P, P, P, P, P, P, P, I64, I64, I64, F, I, I, P]),
         "aaren_append": (I, [P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P]),
@@ -108,6 +118,18 @@ def _on_tensor_device(fn):
 def _check(status: int):
     if status != AAREN_OK:
         raise AarenError(status, lib.aaren_last_error().decode(errors="replace"))
+
+
+_DEBUG = os.environ.get("AAREN_DEBUG", "0") not in ("", "0")
+
+
+def _debug_check(ws, what: str):
+    """With AAREN_DEBUG set: wait for the call and raise if its workspace
+    reports a workgroup that could not take part normally."""
+    if _DEBUG and ws is not None:
+        flags = aaren_workspace_status(ws)
+        if flags:
+            raise AarenError(AAREN_ERR_HIP, f"{what}: workspace error flags {flags:#x}")
 
 
 def _dtype_code(t: torch.dtype) -> int:
@@ -170,6 +192,38 @@ def _workspace(kind: str, nbytes: int, device, zeroed: bool):
 
 # ---- entry points ------------------------------------------------------------
 
+_initialised: set = set()
+
+
+def aaren_init(device=None):
+    """Prepare a GPU (the current one by default) for the calls that keep
+    library state (the layer's rocBLAS handle). Allocates; not under graph
+    capture. Repeated calls do nothing."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    if device in _initialised:
+        return
+    if torch.cuda.is_current_stream_capturing():
+        raise AarenError(AAREN_ERR_UNSUPPORTED,
+                         "aaren_init allocates and cannot run under graph capture")
+    with torch.cuda.device(device):
+        _check(lib.aaren_init())
+    _initialised.add(device)
+
+
+@_on_tensor_device
+def aaren_workspace_status(workspace: torch.Tensor, reset: bool = False) -> int:
+    """The workspace's error flags (0: every scan that used it ran normally;
+    bits 1, 2, 4 as in include/aaren.h); waits for the current stream. With
+    reset, the flags are cleared after they are read."""
+    dev = _need_cuda(workspace)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check(lib.aaren_workspace_status(_ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _ptr(flags), int(bool(reset)), _stream(dev)))
+    return int(flags.item()) & 0xFFFFFFFF
+
+
 def aaren_version() -> int:
     return int(lib.aaren_version())
 
@@ -206,7 +260,8 @@ def aaren_workspace_clear(workspace: torch.Tensor):
 def aaren_scan(q, k, v, scale=None, out_dtype=None, out=None, workspace=None, lse=None,
                return_lse=False):
     """Many-to-many output. q [H,d], k,v [B,H,N,d] -> o [B,H,N,d] (and, with
-    return_lse or a given lse tensor, the log-normaliser [B,H,N] float32)."""
+    return_lse or a given lse tensor, the log-normaliser [B,H,N] float32,
+    through aaren_scan_lse)."""
     dev = _need_cuda(q, k, v, out, workspace, lse)
     B, H, N, d = k.shape
     if q.shape != (H, d) or v.shape != k.shape or q.dtype != k.dtype or v.dtype != k.dtype:
@@ -220,12 +275,25 @@ def aaren_scan(q, k, v, scale=None, out_dtype=None, out=None, workspace=None, ls
         lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
     need = aaren_scan_workspace_size(B, H, N, d)
     ws = workspace if workspace is not None else _workspace("scan", need, dev, True)
-    _check(lib.aaren_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-                          default_scale(d) if scale is None else float(scale),
-                          _dtype_code(k.dtype), _dtype_code(out_dtype),
-                          _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                          _stream(dev)))
+    sc = default_scale(d) if scale is None else float(scale)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    if lse is None:
+        _check(lib.aaren_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, sc,
+                              _dtype_code(k.dtype), _dtype_code(out_dtype), _ptr(ws), wsb,
+                              _stream(dev)))
+    else:
+        if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B,H,N]")
+        _check(lib.aaren_scan_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                  sc, _dtype_code(k.dtype), _dtype_code(out_dtype), _ptr(ws),
+                                  wsb, _stream(dev)))
+    _debug_check(ws, "aaren_scan")
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def aaren_scan_lse(q, k, v, scale=None, out_dtype=None, out=None, workspace=None, lse=None):
+    """aaren_scan with the log-normaliser: returns (o, lse [B,H,N] float32)."""
+    return aaren_scan(q, k, v, scale, out_dtype, out, workspace, lse, return_lse=True)
 
 
 @_on_tensor_device
@@ -233,7 +301,8 @@ def aaren_scan_segmented(q, k, v, offsets, scale=None, out_dtype=None, out=None,
                          lse=None, return_lse=False):
     """Each packed sequence scanned on its own. q [H,d], k,v [T,H,d],
     offsets int64 [num_seqs+1] on the device -> o [T,H,d] (and, with
-    return_lse or a given lse tensor, the log-normaliser [T,H] float32)."""
+    return_lse or a given lse tensor, the log-normaliser [T,H] float32,
+    through aaren_scan_segmented_lse)."""
     dev = _need_cuda(q, k, v, offsets, out, workspace, lse)
     T, H, d = k.shape
     if q.shape != (H, d) or v.shape != k.shape or q.dtype != k.dtype or v.dtype != k.dtype:
@@ -250,13 +319,28 @@ def aaren_scan_segmented(q, k, v, offsets, scale=None, out_dtype=None, out=None,
         lse = torch.empty(T, H, dtype=torch.float32, device=dev)
     need = aaren_scan_segmented_workspace_size(S, T, H, d)
     ws = workspace if workspace is not None else _workspace("scan", need, dev, True)
-    _check(lib.aaren_scan_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                    _ptr(offsets), S, T, H,
-                                    d, default_scale(d) if scale is None else float(scale),
-                                    _dtype_code(k.dtype), _dtype_code(out_dtype), _ptr(ws),
-                                    0 if ws is None else ws.numel() * ws.element_size(),
-                                    _stream(dev)))
+    sc = default_scale(d) if scale is None else float(scale)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    if lse is None:
+        _check(lib.aaren_scan_segmented(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(offsets), S,
+                                        T, H, d, sc, _dtype_code(k.dtype),
+                                        _dtype_code(out_dtype), _ptr(ws), wsb, _stream(dev)))
+    else:
+        if lse.shape != (T, H) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [T,H]")
+        _check(lib.aaren_scan_segmented_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                            _ptr(offsets), S, T, H, d, sc, _dtype_code(k.dtype),
+                                            _dtype_code(out_dtype), _ptr(ws), wsb,
+                                            _stream(dev)))
+    _debug_check(ws, "aaren_scan_segmented")
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def aaren_scan_segmented_lse(q, k, v, offsets, scale=None, out_dtype=None, out=None,
+                             workspace=None, lse=None):
+    """aaren_scan_segmented with the log-normaliser: returns (o, lse [T,H])."""
+    return aaren_scan_segmented(q, k, v, offsets, scale, out_dtype, out, workspace, lse,
+                                return_lse=True)
 
 
 def aaren_scan_backward_workspace_size(B, H, N, d) -> int:
@@ -294,6 +378,7 @@ def aaren_scan_backward(q, k, v, o, dout, lse, scale=None, dq=None, dk=None, dv=
                                    _dtype_code(k.dtype), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(),
                                    _stream(dev)))
+    _debug_check(ws, "aaren_scan_backward")
     return dq, dk, dv
 
 
@@ -389,6 +474,7 @@ def aaren_scan_strided(q, k, v, scale=None, out_dtype=None, out=None, workspace=
                                   _dtype_code(k.dtype), _dtype_code(out.dtype), _ptr(ws),
                                   0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(dev)))
+    _debug_check(ws, "aaren_scan_strided")
     return (out, lse) if (return_lse or lse is not None) else out
 
 
@@ -410,6 +496,7 @@ def aaren_layer_forward(x, w_kv, q, scale=None, out_dtype=None, out=None, worksp
     out_dtype = out_dtype or torch.bfloat16
     if out is None:
         out = torch.empty(B, N, H, d, dtype=out_dtype, device=dev)
+    aaren_init(dev)  # once per device: the projection's rocBLAS handle
     need = aaren_layer_workspace_size(B, N, H, d)
     ws = workspace if workspace is not None else _workspace("layer", need, dev, True)
     _check(lib.aaren_layer_forward(_ptr(x), _ptr(w_kv), _ptr(q), _ptr(out), B, N, Dm, H, d,
@@ -449,6 +536,7 @@ def aaren_scan_segmented_backward(q, k, v, o, dout, lse, offsets, scale=None, dq
         _ptr(dv), S, T, H, d, default_scale(d) if scale is None else float(scale),
         _dtype_code(k.dtype), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(dev)))
+    _debug_check(ws, "aaren_scan_segmented_backward")
     return dq, dk, dv
 
 

@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <mutex>
 #include <unordered_map>
+#include <unordered_set>
 
 #include "layout.h"
 #include "self_attention.h"
@@ -130,9 +131,9 @@ bool capturing(hipStream_t stream)
 
 // The call's epoch: the host's next one, or (under graph capture) 0 after
 // enqueueing the device-side advance of the header's epoch word.
-aaren_status call_epoch(uint32_t *header, hipStream_t stream, uint32_t *epoch)
+aaren_status call_epoch(uint32_t *header, bool captured, hipStream_t stream, uint32_t *epoch)
 {
-    if (!capturing(stream)) {
+    if (!captured) {
         *epoch = next_epoch();
         return AAREN_OK;
     }
@@ -162,14 +163,24 @@ constexpr uint32_t kGroupInterleaved = 8;
 // per workspace, how many counter bytes are known to be zero (all of them for
 // a workspace it has not seen: it was zero-filled, by contract) and clears the
 // counter region before a call that needs more than that.
+// A call captured into a HIP graph runs again at every replay without passing
+// through here, after whatever other calls used the workspace meanwhile. So a
+// captured call always records its counter clear in the graph, and a
+// workspace once used under capture is never taken as clean again: every
+// later call on it clears its counters first.
 std::mutex g_ws_mutex;
 std::unordered_map<const void *, size_t> g_ws_clean;
+std::unordered_set<const void *> g_ws_captured;
 
-aaren_status prepare_counters(void *workspace, size_t need, hipStream_t stream)
+aaren_status prepare_counters(void *workspace, size_t need, bool captured, hipStream_t stream)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (captured)
+        g_ws_captured.insert(workspace);
     auto it = g_ws_clean.find(workspace);
-    const size_t clean = it == g_ws_clean.end() ? SIZE_MAX : it->second;
+    size_t clean = it == g_ws_clean.end() ? SIZE_MAX : it->second;
+    if (g_ws_captured.count(workspace))
+        clean = 0;
     if (need > clean) {
         aaren_status st = hip_status(
             aaren::launch_fill_zero(static_cast<uint8_t *>(workspace) + aaren::kHeaderBytes, need,
@@ -213,6 +224,15 @@ AAREN_API const char *aaren_last_error(void)
     return g_last_error;
 }
 
+AAREN_API aaren_status aaren_init(void)
+{
+    int device = 0;
+    CHECK(hip_status(hipGetDevice(&device), "hipGetDevice"));
+    if (const char *err = aaren::layer_init(device))
+        return fail(AAREN_ERR_HIP, "device %d: %s", device, err);
+    return AAREN_OK;
+}
+
 AAREN_API aaren_status aaren_workspace_clear(void *workspace, size_t workspace_bytes,
                                              void *hip_stream)
 {
@@ -225,6 +245,22 @@ AAREN_API aaren_status aaren_workspace_clear(void *workspace, size_t workspace_b
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     g_ws_clean[workspace] = SIZE_MAX;
     return AAREN_OK;
+}
+
+AAREN_API aaren_status aaren_workspace_status(const void *workspace, size_t workspace_bytes,
+                                              uint32_t *flags, int reset, void *hip_stream)
+{
+    if (!workspace || !flags)
+        return fail(AAREN_ERR_INVALID_ARG, "workspace or flags is NULL");
+    if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(flags) & 3u))
+        return fail(AAREN_ERR_ALIGNMENT, "workspace (16 B) or flags (4 B) is misaligned");
+    if (workspace_bytes < aaren::kHeaderBytes)
+        return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes has no header (%zu bytes)",
+                    workspace_bytes, aaren::kHeaderBytes);
+    return hip_status(
+        aaren::launch_workspace_status(static_cast<uint32_t *>(const_cast<void *>(workspace)),
+                                       flags, reset, static_cast<hipStream_t>(hip_stream)),
+        "workspace status launch");
 }
 
 // ---- dense scan ---------------------------------------------------------------
@@ -319,19 +355,32 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
         fprintf(stderr, "[aaren] scan B=%lld H=%lld N=%lld d=%lld tiles=%lld rows/tile=%d\n",
                 (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles, rows);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    CHECK(prepare_counters(workspace, counter_bytes(B * H), st));
-    CHECK(call_epoch(p.header, st, &p.epoch));
+    const bool cap = capturing(st);
+    CHECK(prepare_counters(workspace, counter_bytes(B * H), cap, st));
+    CHECK(call_epoch(p.header, cap, st, &p.epoch));
     return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, false, st),
                       "scan launch");
 }
 
 }  // namespace
 
-AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, float *lse,
-                                  int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, int64_t B,
+                                  int64_t H, int64_t N, int64_t d, float scale,
                                   aaren_dtype in_dtype, aaren_dtype out_dtype, void *workspace,
                                   size_t workspace_bytes, void *hip_stream)
 {
+    const int64_t s[3] = {H * N * d, N * d, d};
+    return scan_dense(q, k, v, o, nullptr, B, H, N, d, s, s, scale, in_dtype, out_dtype,
+                      workspace, workspace_bytes, hip_stream);
+}
+
+AAREN_API aaren_status aaren_scan_lse(const void *q, const void *k, const void *v, void *o,
+                                      float *lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                                      float scale, aaren_dtype in_dtype, aaren_dtype out_dtype,
+                                      void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    if (!lse)
+        return fail(AAREN_ERR_INVALID_ARG, "lse is NULL (aaren_scan takes no lse)");
     const int64_t s[3] = {H * N * d, N * d, d};
     return scan_dense(q, k, v, o, lse, B, H, N, d, s, s, scale, in_dtype, out_dtype, workspace,
                       workspace_bytes, hip_stream);
@@ -454,8 +503,9 @@ AAREN_API aaren_status aaren_scan_backward(const void *q, const void *k, const v
     if (log_enabled())
         fprintf(stderr, "[aaren] scan_backward B=%lld H=%lld N=%lld d=%lld tiles=%lld\n",
                 (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles);
-    CHECK(prepare_counters(workspace, counter_bytes(B * H), st));
-    CHECK(call_epoch(p.header, st, &p.epoch));
+    const bool cap = capturing(st);
+    CHECK(prepare_counters(workspace, counter_bytes(B * H), cap, st));
+    CHECK(call_epoch(p.header, cap, st, &p.epoch));
     return hip_status(aaren::launch_scan_backward(p, (int)d, false, in_dtype, st),
                       "scan backward launch");
 }
@@ -566,8 +616,9 @@ AAREN_API aaren_status aaren_scan_segmented_backward(
     if (log_enabled())
         fprintf(stderr, "[aaren] scan_segmented_backward S=%lld T=%lld H=%lld d=%lld tiles=%lld\n",
                 (long long)num_seqs, (long long)T, (long long)H, (long long)d, (long long)tiles);
-    CHECK(prepare_counters(workspace, counter_bytes(H), st));
-    CHECK(call_epoch(p.header, st, &p.epoch));
+    const bool cap = capturing(st);
+    CHECK(prepare_counters(workspace, counter_bytes(H), cap, st));
+    CHECK(call_epoch(p.header, cap, st, &p.epoch));
     CHECK(hip_status(aaren::launch_segment_flags(offsets, num_seqs, T, bitmap, words, st),
                      "segment flags launch"));
     return hip_status(aaren::launch_scan_backward(p, (int)d, true, in_dtype, st),
@@ -587,12 +638,12 @@ AAREN_API size_t aaren_scan_segmented_workspace_size(int64_t num_seqs, int64_t t
     return scan_workspace_bytes(H, tiles, ceil_div(total_tokens, 32), d);
 }
 
-AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const void *v, void *o,
-                                            float *lse, const int64_t *offsets, int64_t num_seqs,
-                                            int64_t total_tokens, int64_t H, int64_t d,
-                                            float scale, aaren_dtype in_dtype,
-                                            aaren_dtype out_dtype, void *workspace,
-                                            size_t workspace_bytes, void *hip_stream)
+namespace {
+
+aaren_status scan_packed(const void *q, const void *k, const void *v, void *o, float *lse,
+                         const int64_t *offsets, int64_t num_seqs, int64_t total_tokens, int64_t H,
+                         int64_t d, float scale, aaren_dtype in_dtype, aaren_dtype out_dtype,
+                         void *workspace, size_t workspace_bytes, void *hip_stream)
 {
     if (num_seqs < 0 || total_tokens < 0 || H < 0)
         return fail(AAREN_ERR_INVALID_ARG, "negative size (num_seqs %lld, T %lld, H %lld)",
@@ -663,12 +714,40 @@ AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const 
         fprintf(stderr, "[aaren] scan_segmented S=%lld T=%lld H=%lld d=%lld tiles=%lld\n",
                 (long long)num_seqs, (long long)total_tokens, (long long)H, (long long)d,
                 (long long)tiles);
-    CHECK(prepare_counters(workspace, counter_bytes(H), st));
-    CHECK(call_epoch(p.header, st, &p.epoch));
+    const bool cap = capturing(st);
+    CHECK(prepare_counters(workspace, counter_bytes(H), cap, st));
+    CHECK(call_epoch(p.header, cap, st, &p.epoch));
     CHECK(hip_status(aaren::launch_segment_flags(offsets, num_seqs, total_tokens, bitmap, words, st),
                      "segment flag launch"));
     return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, true, st),
                       "segmented scan launch");
+}
+
+}  // namespace
+
+AAREN_API aaren_status aaren_scan_segmented(const void *q, const void *k, const void *v, void *o,
+                                            const int64_t *offsets, int64_t num_seqs,
+                                            int64_t total_tokens, int64_t H, int64_t d,
+                                            float scale, aaren_dtype in_dtype,
+                                            aaren_dtype out_dtype, void *workspace,
+                                            size_t workspace_bytes, void *hip_stream)
+{
+    return scan_packed(q, k, v, o, nullptr, offsets, num_seqs, total_tokens, H, d, scale,
+                       in_dtype, out_dtype, workspace, workspace_bytes, hip_stream);
+}
+
+AAREN_API aaren_status aaren_scan_segmented_lse(const void *q, const void *k, const void *v,
+                                                void *o, float *lse, const int64_t *offsets,
+                                                int64_t num_seqs, int64_t total_tokens,
+                                                int64_t H, int64_t d, float scale,
+                                                aaren_dtype in_dtype, aaren_dtype out_dtype,
+                                                void *workspace, size_t workspace_bytes,
+                                                void *hip_stream)
+{
+    if (!lse)
+        return fail(AAREN_ERR_INVALID_ARG, "lse is NULL (aaren_scan_segmented takes no lse)");
+    return scan_packed(q, k, v, o, lse, offsets, num_seqs, total_tokens, H, d, scale, in_dtype,
+                       out_dtype, workspace, workspace_bytes, hip_stream);
 }
 
 // ---- RNN step -----------------------------------------------------------------

@@ -22,23 +22,11 @@
 
 namespace {
 
-// One rocBLAS handle per device, created on first use (rocBLAS allocates its
+// One rocBLAS handle per device, created by aaren_init (rocBLAS allocates its
 // own workspace then) and kept for the process; calls through it are
 // serialised because a handle is not thread-safe.
 std::mutex g_blas_mutex;
 std::unordered_map<int, rocblas_handle> g_blas;
-
-rocblas_handle blas_handle(int device)
-{
-    auto it = g_blas.find(device);
-    if (it != g_blas.end())
-        return it->second;
-    rocblas_handle h = nullptr;
-    if (rocblas_create_handle(&h) != rocblas_status_success)
-        return nullptr;
-    g_blas[device] = h;
-    return h;
-}
 
 size_t round256(size_t x)
 {
@@ -48,6 +36,51 @@ size_t round256(size_t x)
 }  // namespace
 
 extern "C" aaren_status aaren_layer_fail(aaren_status s, const char *msg);
+
+namespace aaren {
+
+// Creates the handle and runs one small product of the layer's types and
+// layout through it, so that rocBLAS has loaded its kernels for them before a
+// layer call can be captured into a graph.
+const char *layer_init(int device)
+{
+    std::lock_guard<std::mutex> lock(g_blas_mutex);
+    if (g_blas.count(device))
+        return nullptr;
+    rocblas_handle h = nullptr;
+    if (rocblas_create_handle(&h) != rocblas_status_success)
+        return "rocblas_create_handle failed";
+    constexpr int n = 64;
+    void *buf = nullptr;
+    if (hipMalloc(&buf, 2 * n * n * 2 + n * n * 4) != hipSuccess) {
+        rocblas_destroy_handle(h);
+        return "hipMalloc of the warm-up product failed";
+    }
+    const char *err = nullptr;
+    if (hipMemsetAsync(buf, 0, 2 * n * n * 2 + n * n * 4, nullptr) != hipSuccess ||
+        rocblas_set_stream(h, nullptr) != rocblas_status_success)
+        err = "warm-up product set-up failed";
+    const float alpha = 1.f, beta = 0.f;
+    uint8_t *b8 = static_cast<uint8_t *>(buf);
+    if (!err && rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, n, n, n, &alpha,
+                                b8, rocblas_datatype_bf16_r, n, b8 + n * n * 2,
+                                rocblas_datatype_bf16_r, n, &beta, b8 + 2 * n * n * 2,
+                                rocblas_datatype_f32_r, n, b8 + 2 * n * n * 2,
+                                rocblas_datatype_f32_r, n, rocblas_datatype_f32_r,
+                                rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
+        err = "warm-up product failed";
+    if (hipStreamSynchronize(nullptr) != hipSuccess && !err)
+        err = "warm-up product did not complete";
+    hipFree(buf);
+    if (err) {
+        rocblas_destroy_handle(h);
+        return err;
+    }
+    g_blas[device] = h;
+    return nullptr;
+}
+
+}  // namespace aaren
 
 AAREN_API size_t aaren_layer_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d)
 {
@@ -99,19 +132,14 @@ AAREN_API aaren_status aaren_layer_forward(const void *x, const void *w_kv, cons
         if (hipGetDevice(&device) != hipSuccess)
             return aaren_layer_fail(AAREN_ERR_HIP, "hipGetDevice failed");
         std::lock_guard<std::mutex> lock(g_blas_mutex);
-        // a handle allocates device memory when it is created, which a stream
-        // being captured into a graph does not allow: the first call on a
-        // device must be an eager one
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        if (g_blas.find(device) == g_blas.end() &&
-            hipStreamIsCapturing(static_cast<hipStream_t>(hip_stream), &cap) == hipSuccess &&
-            cap == hipStreamCaptureStatusActive)
+        // the handle (whose creation allocates) comes from aaren_init, so
+        // this call allocates nothing and may be captured into a graph
+        auto it = g_blas.find(device);
+        if (it == g_blas.end())
             return aaren_layer_fail(AAREN_ERR_UNSUPPORTED,
-                                    "the first layer call on a device cannot be captured into a "
-                                    "graph (it creates the rocBLAS handle); call it once eagerly");
-        rocblas_handle h = blas_handle(device);
-        if (!h)
-            return aaren_layer_fail(AAREN_ERR_HIP, "rocblas_create_handle failed");
+                                    "aaren_init has not been called on this device (it creates "
+                                    "the layer's rocBLAS handle)");
+        rocblas_handle h = it->second;
         if (rocblas_set_stream(h, static_cast<hipStream_t>(hip_stream)) != rocblas_status_success)
             return aaren_layer_fail(AAREN_ERR_HIP, "rocblas_set_stream failed");
         // row-major KV[rows][cols] = x[rows][Dm] W[Dm][cols], i.e. column-major

@@ -13,10 +13,12 @@ namespace aaren {
 
 // ---- scan workspace ---------------------------------------------------------
 // [ header: 256 B ][ ticket counters ][ segment-start bitmap (segmented only) ][ tile slots ]
-// header[kError] : set (never cleared by a call) when a tile gave up waiting
-//                  for its predecessors or drew a ticket out of range -- only
+// header[kError] : bits set (never cleared by a call) when a tile drew a
+//                  ticket out of range (1), walked past the end of its stream
+//                  (2) or gave up waiting for its predecessors (4) -- only
 //                  possible with a workspace that was not zero-filled before
-//                  first use or was shared by overlapping calls.
+//                  first use or was shared by overlapping calls;
+//                  aaren_workspace_status reads (and may clear) it.
 // Ticket counters: one per stream, each in its own 128-byte line. A tile's
 //   workgroup draws its position along the stream from its stream's counter
 //   with a wrapping increment, so the counter is back at 0 when the call ends.
@@ -188,9 +190,13 @@ hipError_t launch_state_init(float *m, float *u, float *w, int64_t units, int64_
                              hipStream_t stream);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_epoch_advance(uint32_t *header, hipStream_t stream);
+hipError_t launch_workspace_status(uint32_t *header, uint32_t *out, int reset, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams &p, int D, aaren_dtype in, aaren_dtype out,
                          hipStream_t stream);
 int reduce_rows_per_iteration(int D, aaren_dtype in);
+// Creates the device's rocBLAS handle for the layer if it has none; returns
+// null or a description of the failure.
+const char *layer_init(int device);
 hipError_t launch_scan_backward(const BackwardParams &p, int D, bool segmented, aaren_dtype in,
                                 hipStream_t stream);
 

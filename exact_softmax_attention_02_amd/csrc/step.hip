@@ -289,6 +289,23 @@ hipError_t launch_epoch_advance(uint32_t *header, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Copy a workspace's error word to *out, then clear it if asked.
+__global__ __launch_bounds__(64) void workspace_status_kernel(uint32_t *header, uint32_t *out,
+                                                              int reset)
+{
+    if (threadIdx.x == 0) {
+        *out = __hip_atomic_load(header + kError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (reset)
+            __hip_atomic_store(header + kError, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+hipError_t launch_workspace_status(uint32_t *header, uint32_t *out, int reset, hipStream_t stream)
+{
+    hipLaunchKernelGGL(workspace_status_kernel, dim3(1), dim3(64), 0, stream, header, out, reset);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t stream)
 {
     hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for((int64_t)(bytes / 16) + 1)), dim3(256), 0,

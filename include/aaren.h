@@ -31,10 +31,9 @@
  *   is (m = -inf, u = 0, w = 0).
  *
  * Conventions:
- *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing (one exception: the first aaren_layer_forward call on
- *    a device creates a rocBLAS handle, which allocates once) and keeps no
- *    pointer after a call's work completes.
+ *  - All tensor pointers are DEVICE pointers owned by the caller; no call
+ *    allocates except aaren_init (the layer's rocBLAS handle), and the library
+ *    keeps no pointer after a call's work completes.
  *  - Tensors are dense, row-major, in the shapes given (aaren_scan_strided
  *    takes explicit strides); q, k and v share `in_dtype` unless a call says
  *    otherwise; every tensor base pointer must be 16-byte aligned.
@@ -52,16 +51,14 @@
  *    same or different devices and streams, provided calls that can run at
  *    the same time (on different streams) use different workspaces and
  *    outputs. Library state shared between calls (the epoch counter, the
- *    record of cleared workspace bytes, the layer's rocBLAS handles) is
- *    guarded.
+ *    record of cleared workspace bytes and of captured workspaces, the
+ *    layer's rocBLAS handles) is guarded.
  *  - Environment: AAREN_LOG=1 prints each call's launch geometry to stderr;
  *    AAREN_STRESS=1 (tests only, read at every call) makes the scans and
  *    their gradients pause tiles at random to perturb the order in which
  *    tiles exchange states; results are unchanged, only slower.
- *  - HIP graphs: every call may be captured for replay; aaren_layer_forward
- *    only after one eager call on the device (its first call creates the
- *    rocBLAS handle, which allocates; captured first, it returns
- *    UNSUPPORTED and enqueues nothing).
+ *  - HIP graphs: every call but aaren_init may be captured for replay
+ *    (aaren_layer_forward once aaren_init has run on the device).
  *    The scans (aaren_scan, aaren_scan_strided, aaren_scan_segmented) and
  *    their gradients tag the states their workgroups exchange with an epoch:
  *    an eager call takes it from a counter on the host; a call made while its
@@ -71,6 +68,9 @@
  *    of its own. Eager and captured calls may share a workspace (the two
  *    kinds of epoch are drawn from disjoint ranges), but replays and calls
  *    on one workspace must not overlap in time, like any two calls on it.
+ *    A captured scan also records the clearing of its ticket counters, and
+ *    every later call on a workspace once used under capture clears its own
+ *    (a replay can follow any call of another shape on that workspace).
  *    No call enqueues a memset.
  */
 #ifndef AAREN_H
@@ -106,6 +106,16 @@ const char *aaren_status_string(aaren_status s);
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char *aaren_last_error(void);
 
+/* ---- set-up ------------------------------------------------------------------
+ * Prepares the calling thread's current HIP device for the calls that keep
+ * state in the library: creates the rocBLAS handle aaren_layer_forward runs
+ * its projection with (rocBLAS allocates its workspace then). Call it once per
+ * device, before the first aaren_layer_forward there, and never while a stream
+ * of the process is being captured into a graph (it allocates); further calls
+ * on an initialised device do nothing. It is the only call that allocates.
+ * HIP if the handle cannot be created. */
+aaren_status aaren_init(void);
+
 /* ---- workspaces ------------------------------------------------------------
  * The scans carry the running state across tiles of a sequence through a
  * caller-owned workspace (per-stream ticket counters and per-tile published
@@ -127,21 +137,50 @@ const char *aaren_last_error(void);
  */
 aaren_status aaren_workspace_clear(void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* Whether the scans that used a workspace ran as they should. The scans
+ * (dense, strided, packed) and their gradients note in the workspace header
+ * when one of their workgroups could not take part normally, and then
+ * their outputs are wrong: bit 0 (value 1), a workgroup drew a position
+ * along its sequence outside the sequence (its ticket counter was not zero
+ * when the call began); bit 1 (2), a workgroup walked past the first or
+ * last tile of its sequence; bit 2 (4), a workgroup gave up after waiting
+ * about a second for an earlier tile's state. None of them happens with a
+ * workspace used by the contract above; each points to one that was not
+ * zero-filled before first use, was written between calls, or was used by
+ * calls that overlapped in time. The word accumulates over calls.
+ * This call enqueues on `hip_stream` a copy of the word into `*flags` (a
+ * DEVICE uint32, 4-byte aligned; read it after the stream's work is done)
+ * and, when `reset` is nonzero, clears the word after copying it. It does
+ * not synchronise. INVALID_ARG for NULL pointers, ALIGNMENT for a misaligned
+ * workspace or flags, WORKSPACE for a workspace smaller than its 256-byte
+ * header. */
+aaren_status aaren_workspace_status(const void *workspace, size_t workspace_bytes,
+                                    uint32_t *flags, int reset, void *hip_stream);
+
 /* ---- many-to-many scan, dense batch ----------------------------------------
  * Many-to-many output of "Attention as an RNN" (abstract item (3): attention's
- * many-to-many RNN output by a parallel prefix scan), one query per head.
+ * many-to-many RNN output by a parallel prefix scan; the form that lets the
+ * module of item (4) be (i) trained in parallel), one query per head.
  *   q [H,d], k [B,H,N,d], v [B,H,N,d]  (in_dtype)
  *   o [B,H,N,d]                         (out_dtype), o[b,h,i] = attention of
  *                                       q[h] over pairs 0..i of (b,h)
- *   lse [B,H,N] float32 or NULL: the log-normaliser L_i = ln sum_{j<=i} e^{s_j}
- *                                of every row (what aaren_scan_backward needs)
  * B*H*N == 0 is a no-op. Returns WORKSPACE if workspace_bytes is below
  * aaren_scan_workspace_size(B,H,N,d). */
 size_t aaren_scan_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d);
-aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, float *lse,
+aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o,
                         int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                         aaren_dtype in_dtype, aaren_dtype out_dtype,
                         void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* aaren_scan that also writes, in the same pass,
+ *   lse [B,H,N] float32 (not NULL: INVALID_ARG): the log-normaliser
+ *   L_i = ln sum_{j<=i} e^{s_j} of every row, what aaren_scan_backward takes.
+ * Same workspace, statuses and outputs as aaren_scan otherwise; lse must be
+ * 4-byte aligned (ALIGNMENT). */
+aaren_status aaren_scan_lse(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                            aaren_dtype in_dtype, aaren_dtype out_dtype,
+                            void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* ---- gradients of the dense many-to-many scan -------------------------------
  * "Attention as an RNN" (review, proposed method) presents the many-to-many
@@ -151,7 +190,7 @@ aaren_status aaren_scan(const void *q, const void *k, const void *v, void *o, fl
  *   ds_i = <dv_i, v_i> - sum_{k>=i} p_ki <g_k, o_k>
  *   dk_i = scale ds_i q_h,  dq_h = scale sum_{b,i} ds_i k_i  (summed over the batch)
  *   q [H,d], k, v, dout [B,H,N,d]  in_dtype (float32 or bfloat16)
- *   o [B,H,N,d] float32: the forward's output (aaren_scan with out_dtype F32)
+ *   o [B,H,N,d] float32: the forward's output (aaren_scan_lse, out_dtype F32)
  *   lse [B,H,N] float32: the forward's log-normaliser
  *   dq [H,d], dk, dv [B,H,N,d] float32 outputs
  * One pass over K, V, O and dout; dq is reproducible bit for bit. bfloat16
@@ -190,15 +229,26 @@ aaren_status aaren_scan_strided(const void *q, const void *k, const void *v, voi
  *   offsets[num_seqs] = T; sequence s holds tokens offsets[s] .. offsets[s+1]-1
  *   (empty sequences allowed).
  * The host cannot read device offsets, so only their count is validated; a
- * decreasing array or one that does not end at T gives unspecified results. */
+ * decreasing array or one that does not end at T gives unspecified results.
+ * num_seqs = 0 with T = 0 is a no-op; tokens without sequences INVALID_ARG;
+ * offsets must be 8-byte aligned. */
 size_t aaren_scan_segmented_workspace_size(int64_t num_seqs, int64_t total_tokens,
                                            int64_t H, int64_t d);
 aaren_status aaren_scan_segmented(const void *q, const void *k, const void *v, void *o,
-                                  float *lse /* [T,H] or NULL */,
                                   const int64_t *offsets, int64_t num_seqs,
                                   int64_t total_tokens, int64_t H, int64_t d, float scale,
                                   aaren_dtype in_dtype, aaren_dtype out_dtype,
                                   void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* aaren_scan_segmented that also writes lse [T,H] float32 (not NULL), the
+ * log-normaliser of every row within its own sequence, as aaren_scan_lse
+ * does for a dense batch (what aaren_scan_segmented_backward takes). */
+aaren_status aaren_scan_segmented_lse(const void *q, const void *k, const void *v, void *o,
+                                      float *lse, const int64_t *offsets, int64_t num_seqs,
+                                      int64_t total_tokens, int64_t H, int64_t d, float scale,
+                                      aaren_dtype in_dtype, aaren_dtype out_dtype,
+                                      void *workspace, size_t workspace_bytes,
+                                      void *hip_stream);
 
 /* ---- constant-memory RNN step ----------------------------------------------
  * "Attention as an RNN" (abstract item (4)(ii) and method: update with new
@@ -241,7 +291,7 @@ aaren_status aaren_append(const void *q, const void *k, const void *v,
  * Gradients of aaren_scan_segmented: each sequence's gradients are those of
  * a dense scan of that sequence alone; dq adds every sequence's.
  *   q [H,d]; k, v, dout [T,H,d] token-major, in_dtype (float32 or bfloat16);
- *   o [T,H,d] float32 and lse [T,H] (aaren_scan_segmented's outputs);
+ *   o [T,H,d] float32 and lse [T,H] (aaren_scan_segmented_lse's outputs);
  *   offsets [num_seqs+1] int64 device array as for the forward;
  *   dq [H,d], dk, dv [T,H,d] float32 outputs.
  * Workspace as for aaren_scan_backward (zero-filled once before first use;
@@ -287,8 +337,9 @@ aaren_status aaren_reduce(const void *q, const void *k, const void *v, void *o,
  * o [B,N,H,d] (out_dtype; a stacked layer takes o, bf16, as its x with
  * Dm = H*d). The workspace (aaren_layer_workspace_size) holds K|V in fp32
  * and the scan's state; zero-fill it once before first use, as for
- * aaren_scan. The first call on a device creates a rocBLAS handle (rocBLAS
- * allocates its own workspace then); later calls allocate nothing.
+ * aaren_scan. The projection runs through the rocBLAS handle aaren_init
+ * created for the device; without it the call returns UNSUPPORTED and
+ * enqueues nothing. It allocates nothing.
  * B*N*H = 0: OK, nothing done. Dm = 0 with rows: INVALID_ARG. Sizes beyond
  * the 32-bit GEMM interface: UNSUPPORTED. A GEMM failure: HIP. */
 size_t aaren_layer_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d);

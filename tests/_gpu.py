@@ -42,3 +42,38 @@ def check(got: torch.Tensor, ref: np.ndarray, tol: float, what: str):
 def scan_header_error(ws: torch.Tensor) -> int:
     """The workspace's error word (0 unless a tile gave up waiting)."""
     return int(ws[12:16].view(torch.int32).item())
+
+
+# dq = scale * sum_i ds_i k_i adds B*N (or T) terms per head, in a fixed tree
+# of about 100 levels (8 rows per lane, 16 lane groups, the tiles' partials).
+# With rounding errors of independent signs the sum's error is about
+# sqrt(depth) 2^-24 times the root-sum-square of the terms, and the sum itself
+# is of that size for independent inputs: a scaled error of order 1e-6, as
+# measured. 1e-4 leaves two orders of magnitude of margin and is still far
+# below what losing one lane group's 8-row partial does at the dense
+# workload's shape (about 1e-2; test_gpu_workloads shows the check failing
+# on such a planted loss).
+DQ_TOL = 1e-4
+
+
+def gpu_scaled_err(got: torch.Tensor, ref: np.ndarray) -> float:
+    """oracle.max_scaled_err, evaluated on the device in float64 (the
+    full-size checks compare billions of elements; the host is slow at it).
+    Elements NaN on both sides count as equal; any other NaN fails."""
+    torch.cuda.synchronize()
+    if got.numel() == 0:
+        return 0.0
+    r = torch.from_numpy(np.ascontiguousarray(ref, dtype=np.float64)).to(got.device)
+    g = got.double()
+    if g.shape != r.shape:
+        raise ValueError(f"shape mismatch {tuple(g.shape)} vs {tuple(r.shape)}")
+    err = (g - r).abs_().div_(r.abs().add_(1.0))
+    err = torch.where(torch.isnan(g) & torch.isnan(r), torch.zeros_like(err), err)
+    if bool(torch.isnan(err).any()):
+        return float("inf")
+    return float(err.max())
+
+
+def progress(msg: str):
+    """A line per finished part of a long check (flushed)."""
+    print(msg, file=sys.stderr, flush=True)

@@ -70,7 +70,7 @@ int main(int argc, char **argv)
         return 1;
 
     const float scale = 0.125f; /* 1 / sqrt(64) */
-    const aaren_status st = aaren_scan(dq, dk, dv, dout, NULL, B, H, N, D, scale, AAREN_F32,
+    const aaren_status st = aaren_scan(dq, dk, dv, dout, B, H, N, D, scale, AAREN_F32,
                                        AAREN_F32, ws, wsb, NULL);
     if (st != AAREN_OK) {
         fprintf(stderr, "aaren_scan: %s (%s)\n", aaren_status_string(st), aaren_last_error());

@@ -64,7 +64,9 @@ S = {"ok": 0, "arg": 1, "unsup": 2, "align": 3, "ws": 4}
 
 
 def scan(q=A, k=A, v=A, o=A, lse=None, B=1, H=1, N=16, d=64, ind=0, outd=0, ws=A, wsb=1 << 30):
-    return L.aaren_scan(q, k, v, o, lse, B, H, N, d, 0.125, ind, outd, ws, wsb, None)
+    if lse is None:
+        return L.aaren_scan(q, k, v, o, B, H, N, d, 0.125, ind, outd, ws, wsb, None)
+    return L.aaren_scan_lse(q, k, v, o, lse, B, H, N, d, 0.125, ind, outd, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -77,6 +79,16 @@ def scan(q=A, k=A, v=A, o=A, lse=None, B=1, H=1, N=16, d=64, ind=0, outd=0, ws=A
 def test_scan_validation(kw, status):
     assert scan(**kw) == S[status]
     assert aaren.aaren_last_error()
+    if "lse" not in kw:  # the lse form validates the shared arguments alike
+        assert scan(lse=A, **kw) == S[status]
+
+
+def test_lse_forms_need_lse():
+    assert L.aaren_scan_lse(A, A, A, A, None, 1, 1, 16, 64, 0.125, 0, 0, A, 1 << 30,
+                            None) == S["arg"]
+    assert "lse" in aaren.aaren_last_error()
+    assert L.aaren_scan_segmented_lse(A, A, A, A, None, A, 2, 10, 1, 64, 0.125, 0, 0, A,
+                                      1 << 30, None) == S["arg"]
 
 
 def test_scan_empty_is_a_noop():
@@ -85,7 +97,10 @@ def test_scan_empty_is_a_noop():
 
 
 def seg(offs=A, S_=2, T=10, H=1, d=64, q=A, wsb=1 << 30, lse=None):
-    return L.aaren_scan_segmented(q, A, A, A, lse, offs, S_, T, H, d, 0.125, 0, 0, A, wsb, None)
+    if lse is None:
+        return L.aaren_scan_segmented(q, A, A, A, offs, S_, T, H, d, 0.125, 0, 0, A, wsb, None)
+    return L.aaren_scan_segmented_lse(q, A, A, A, lse, offs, S_, T, H, d, 0.125, 0, 0, A, wsb,
+                                      None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -95,6 +110,17 @@ def seg(offs=A, S_=2, T=10, H=1, d=64, q=A, wsb=1 << 30, lse=None):
 ])
 def test_segmented_validation(kw, status):
     assert seg(**kw) == S[status]
+    if "lse" not in kw:
+        assert seg(lse=A, **kw) == S[status]
+
+
+def test_workspace_status_validation():
+    ws = L.aaren_workspace_status
+    assert ws(None, 4096, A, 0, None) == S["arg"]
+    assert ws(A, 4096, None, 0, None) == S["arg"]
+    assert ws(A + 8, 4096, A, 0, None) == S["align"]
+    assert ws(A, 4096, A + 2, 0, None) == S["align"]
+    assert ws(A, 255, A, 0, None) == S["ws"]
 
 
 def test_segmented_empty_is_a_noop():

@@ -57,3 +57,16 @@ def test_c_client_scan_matches_oracle(tmp_path):
     err = oracle.max_scaled_err(o, ref)
     print(f"C client: {r.stdout.strip()}; max scaled err {err:.2e}")
     assert err <= 1e-5, err
+
+
+def test_header_matches_the_stated_prototypes(tmp_path):
+    """tests/abi_contract.c re-declares the boundary's entry points with the
+    prototypes the scope table states; C rejects a second declaration of a
+    different type, so this compiles only if the header agrees with them."""
+    if shutil.which("gcc") is None:
+        pytest.skip("needs gcc")
+    r = subprocess.run(
+        ["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
+         "-I", os.path.join(ROOT, "include"), os.path.join(HERE, "abi_contract.c")],
+        capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

@@ -41,9 +41,9 @@ def test_scan_rejections_touch_nothing():
     o, lse = _filled(B, H, N, d), _filled(B, H, N)
     need = aaren.aaren_scan_workspace_size(B, H, N, d)
     ws = torch.zeros(need, dtype=torch.uint8, device=dev())
-    call = lambda **kw: L.aaren_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
-                                     kw.get("d", d), 0.125, 0, 0, _ptr(ws), kw.get("wsb", need),
-                                     _stream())
+    call = lambda **kw: L.aaren_scan_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
+                                         kw.get("d", d), 0.125, 0, 0, _ptr(ws),
+                                         kw.get("wsb", need), _stream())
     assert call(wsb=need - 1) == aaren.AAREN_ERR_WORKSPACE
     assert "workspace" in aaren.aaren_last_error()
     assert call(d=96) == aaren.AAREN_ERR_UNSUPPORTED
@@ -74,7 +74,7 @@ def test_backward_and_segmented_rejections_touch_nothing():
     need_s = aaren.aaren_scan_segmented_workspace_size(2, T, H, d)
     ws_s = torch.zeros(need_s, dtype=torch.uint8, device=dev())
     bad = ctypes.c_void_p(offs.data_ptr() + 4)
-    st = L.aaren_scan_segmented(_ptr(q), _ptr(kp), _ptr(vp), _ptr(out), None, bad, 2, T, H, d,
+    st = L.aaren_scan_segmented(_ptr(q), _ptr(kp), _ptr(vp), _ptr(out), bad, 2, T, H, d,
                                 0.125, 0, 0, _ptr(ws_s), need_s, _stream())
     assert st == aaren.AAREN_ERR_ALIGNMENT
     assert _untouched(out)

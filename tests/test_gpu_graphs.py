@@ -136,6 +136,46 @@ def test_dense_scan_in_a_graph():
         assert scan_header_error(ws) == 0
 
 
+def test_graph_replays_between_calls_of_other_shapes():
+    """A scan of 256 streams captured into a graph, with eager scans of 8
+    streams on the same workspace before every replay: the small calls' tile
+    states cover the bytes the large call counts tickets in, so each replay
+    must clear its own counters (the capture records that), and the eager
+    calls after a replay must clear theirs. Every replay and every eager call
+    equals the result on a workspace of its own, and the error word stays
+    clear."""
+    announce("graph: 256-stream scan replayed between 8-stream eager scans")
+    d, N = 64, 1024
+    g = torch.Generator(device=dev()).manual_seed(34)
+    qb, kb, vb = (torch.randn(*s_, generator=g, device=dev())
+                  for s_ in ((8, d), (32, 8, N, d), (32, 8, N, d)))
+    qs, ks, vs = (torch.randn(*s_, generator=g, device=dev())
+                  for s_ in ((8, d), (1, 8, N, d), (1, 8, N, d)))
+    ref_b = aaren.aaren_scan(qb, kb, vb, workspace=torch.zeros(
+        aaren.aaren_scan_workspace_size(32, 8, N, d), dtype=torch.uint8, device=dev())).clone()
+    ref_s = aaren.aaren_scan(qs, ks, vs, workspace=torch.zeros(
+        aaren.aaren_scan_workspace_size(1, 8, N, d), dtype=torch.uint8, device=dev())).clone()
+    ws = torch.zeros(aaren.aaren_scan_workspace_size(32, 8, N, d), dtype=torch.uint8,
+                     device=dev())
+    ob = torch.empty_like(kb)
+    aaren.aaren_scan(qb, kb, vb, out=ob, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        aaren.aaren_scan(qb, kb, vb, out=ob, workspace=ws)
+    for _ in range(REPLAYS):
+        assert torch.equal(aaren.aaren_scan(qs, ks, vs, workspace=ws), ref_s)
+        ob.zero_()
+        _noise()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ob, ref_b)
+        assert aaren.aaren_workspace_status(ws) == 0
+        assert torch.equal(aaren.aaren_scan(qs, ks, vs, workspace=ws), ref_s)
+        assert torch.equal(aaren.aaren_scan(qb, kb, vb, workspace=ws), ref_b)
+        assert aaren.aaren_workspace_status(ws) == 0
+
+
 def test_packed_scan_in_a_graph():
     announce("graph: packed scan")
     H, d = 2, 128
@@ -224,35 +264,48 @@ def test_layer_in_a_graph():
         assert torch.equal(o, ref)
 
 
-_FIRST_CAPTURED = """
-import torch, exact_softmax_attention_02_amd as aaren, workloads
+_INIT_THEN_CAPTURE = """
+import ctypes, torch, exact_softmax_attention_02_amd as aaren, workloads
 dev = torch.device("cuda:0")
 x, w, q = workloads.layer_inputs(1, 300, 128, 2, 64, 1, 43, device=dev)
+w, q = w[0], q[0]
 wsp = torch.zeros(aaren.aaren_layer_workspace_size(1, 300, 2, 64), dtype=torch.uint8, device=dev)
-o = torch.empty(1, 300, 2, 64, dtype=torch.bfloat16, device=dev)
-graph = torch.cuda.CUDAGraph()
-try:
-    with torch.cuda.graph(graph):
-        aaren.aaren_layer_forward(x, w[0], q[0], out=o, workspace=wsp)
-    print("captured")
-except aaren.AarenError as e:
-    assert e.status == aaren.AAREN_ERR_UNSUPPORTED, e.status
-    print("refused:", e)
-aaren.aaren_layer_forward(x, w[0], q[0], out=o, workspace=wsp)   # eager calls still work
+o = torch.full((1, 300, 2, 64), 7.0, dtype=torch.bfloat16, device=dev)
+P = lambda t: ctypes.c_void_p(t.data_ptr())
+st = aaren.lib.aaren_layer_forward(P(x), P(w), P(q), P(o), 1, 300, 128, 2, 64, 0.125,
+                                   aaren.AAREN_BF16, P(wsp), wsp.numel(), None)
 torch.cuda.synchronize()
-print("eager after refusal ok")
+assert st == aaren.AAREN_ERR_UNSUPPORTED, st
+assert "aaren_init" in aaren.aaren_last_error()
+assert bool((o == 7.0).all())
+print("refused before aaren_init")
+aaren.aaren_init()
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph):
+    aaren.aaren_layer_forward(x, w, q, out=o, workspace=wsp)
+print("first layer call captured")
+for _ in range(3):
+    o.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    ref = aaren.aaren_layer_forward(x, w, q, workspace=wsp)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+print("replays equal eager calls")
 """
 
 
-def test_layer_first_call_captured_is_refused():
-    """In a process whose first layer call is made under capture the call is
-    refused with UNSUPPORTED (creating the rocBLAS handle allocates), enqueues
-    nothing, and later eager calls work. Run in a child process so that no
-    earlier layer call of the test session has created the handle."""
-    announce("graph: layer first call under capture (child process)")
+def test_layer_needs_init_and_is_captured_after_it():
+    """In a fresh process a layer call before aaren_init is refused with
+    UNSUPPORTED and touches nothing; after aaren_init (which creates the
+    rocBLAS handle) the very first layer call can be captured, and its
+    replays equal eager calls. A child process, so that no earlier call of
+    the test session has initialised the device."""
+    announce("graph: layer refused before aaren_init, captured after it (child process)")
     env = dict(os.environ, PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
-    r = subprocess.run([sys.executable, "-c", _FIRST_CAPTURED], capture_output=True, text=True,
-                       env=env, timeout=120, cwd=ROOT)
+    r = subprocess.run([sys.executable, "-c", _INIT_THEN_CAPTURE], capture_output=True,
+                       text=True, env=env, timeout=120, cwd=ROOT)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert "refused:" in r.stdout and "cannot be captured" in r.stdout, r.stdout
-    assert "eager after refusal ok" in r.stdout
+    for line in ("refused before aaren_init", "first layer call captured",
+                 "replays equal eager calls"):
+        assert line in r.stdout, r.stdout
