@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <unordered_map>
 #include <unordered_set>
@@ -49,9 +50,22 @@ bool aligned16(const void *p)
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-bool dtype_ok(aaren_dtype t)
+// A dtype argument's value, read from its bytes: a C caller may pass any int,
+// and a value outside the enumerators must not be loaded as the enum. The
+// checks below therefore take dtypes by reference and read them this way.
+static_assert(sizeof(aaren_dtype) == sizeof(int), "aaren_dtype is passed as an int");
+
+int dtype_code(const aaren_dtype &t)
 {
-    return t == AAREN_F32 || t == AAREN_BF16;
+    int v;
+    std::memcpy(&v, &t, sizeof v);
+    return v;
+}
+
+bool dtype_ok(const aaren_dtype &t)
+{
+    const int v = dtype_code(t);
+    return v == AAREN_F32 || v == AAREN_BF16;
 }
 
 // a*b*... without overflow past 2^62, else -1
@@ -75,13 +89,14 @@ aaren_status hip_status(hipError_t e, const char *what)
     return fail(AAREN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-aaren_status check_common(int64_t d, aaren_dtype in, aaren_dtype out)
+aaren_status check_common(int64_t d, const aaren_dtype &in, const aaren_dtype &out)
 {
     if (d != 64 && d != 128)
         return fail(AAREN_ERR_UNSUPPORTED, "d = %lld: supported head dimensions are 64 and 128",
                     (long long)d);
     if (!dtype_ok(in) || !dtype_ok(out))
-        return fail(AAREN_ERR_UNSUPPORTED, "unknown dtype (in %d, out %d)", (int)in, (int)out);
+        return fail(AAREN_ERR_UNSUPPORTED, "unknown dtype (in %d, out %d)", dtype_code(in),
+                    dtype_code(out));
     return AAREN_OK;
 }
 
@@ -141,9 +156,10 @@ aaren_status call_epoch(uint32_t *header, bool captured, hipStream_t stream, uin
     return hip_status(aaren::launch_epoch_advance(header, stream), "epoch advance launch");
 }
 
+// a / b rounded up, for a >= 0 and b > 0 (no intermediate beyond a)
 int64_t ceil_div(int64_t a, int64_t b)
 {
-    return (a + b - 1) / b;
+    return a / b + (a % b != 0);
 }
 
 // Consecutive workgroups per stream (see scan.hip). Measured on MI355X with
@@ -208,7 +224,11 @@ AAREN_API int aaren_version(void)
 
 AAREN_API const char *aaren_status_string(aaren_status s)
 {
-    switch (s) {
+    // a C caller may pass any int: read its bits, not the enum (whose range
+    // in C++ ends at 7)
+    int code;
+    std::memcpy(&code, &s, sizeof code);
+    switch (code) {
     case AAREN_OK: return "ok";
     case AAREN_ERR_INVALID_ARG: return "invalid argument";
     case AAREN_ERR_UNSUPPORTED: return "unsupported";
@@ -279,10 +299,11 @@ namespace {
 
 // The dense scan with explicit element strides {batch, head, row} for k/v and
 // for o (lse is always [B,H,N]).
+// kvs == os == nullptr: contiguous [B,H,N,d] tensors.
 aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, float *lse,
-                        int64_t B, int64_t H, int64_t N, int64_t d, const int64_t kvs[3],
-                        const int64_t os[3], float scale, aaren_dtype in_dtype,
-                        aaren_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                        int64_t B, int64_t H, int64_t N, int64_t d, const int64_t *kv_strides,
+                        const int64_t *o_strides, float scale, const aaren_dtype &in_dtype,
+                        const aaren_dtype &out_dtype, void *workspace, size_t workspace_bytes,
                         void *hip_stream)
 {
     if (B < 0 || H < 0 || N < 0)
@@ -294,11 +315,24 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
         return fail(AAREN_ERR_UNSUPPORTED, "B*H*N*d overflows");
     if (elems == 0)
         return AAREN_OK;
+    const int64_t dense[3] = {H * N * d, N * d, d};  // no overflow: B*H*N*d fits
+    const int64_t *kvs = kv_strides ? kv_strides : dense, *os = o_strides ? o_strides : dense;
     const int64_t in_bytes = in_dtype == AAREN_F32 ? 4 : 2, out_bytes = out_dtype == AAREN_F32 ? 4 : 2;
+    // the last row's byte offset, b*sb + h*sh + n*sn with every index at its
+    // largest, must fit in 63 bits
+    const int64_t last[3] = {B - 1, H - 1, N - 1};
+    int64_t kv_end = 0, o_end = 0;
     for (int i = 0; i < 3; ++i) {
         if (kvs[i] < 0 || os[i] < 0)
             return fail(AAREN_ERR_INVALID_ARG, "negative stride");
-        if ((kvs[i] * in_bytes) % 16 || (os[i] * out_bytes) % 16)
+        const int64_t kb = mul_checked({kvs[i], in_bytes}), ob = mul_checked({os[i], out_bytes});
+        const int64_t kt = mul_checked({last[i], kb}), ot = mul_checked({last[i], ob});
+        if (kb < 0 || ob < 0 || kt < 0 || ot < 0 || kt > (int64_t(1) << 62) - kv_end ||
+            ot > (int64_t(1) << 62) - o_end)
+            return fail(AAREN_ERR_UNSUPPORTED, "strides address beyond 2^62 bytes");
+        kv_end += kt;
+        o_end += ot;
+        if (kb % 16 || ob % 16)
             return fail(AAREN_ERR_ALIGNMENT, "a stride is not a multiple of 16 bytes");
     }
     CHECK(check_ptr(q, "q"));
@@ -369,9 +403,8 @@ AAREN_API aaren_status aaren_scan(const void *q, const void *k, const void *v, v
                                   aaren_dtype in_dtype, aaren_dtype out_dtype, void *workspace,
                                   size_t workspace_bytes, void *hip_stream)
 {
-    const int64_t s[3] = {H * N * d, N * d, d};
-    return scan_dense(q, k, v, o, nullptr, B, H, N, d, s, s, scale, in_dtype, out_dtype,
-                      workspace, workspace_bytes, hip_stream);
+    return scan_dense(q, k, v, o, nullptr, B, H, N, d, nullptr, nullptr, scale, in_dtype,
+                      out_dtype, workspace, workspace_bytes, hip_stream);
 }
 
 AAREN_API aaren_status aaren_scan_lse(const void *q, const void *k, const void *v, void *o,
@@ -381,9 +414,8 @@ AAREN_API aaren_status aaren_scan_lse(const void *q, const void *k, const void *
 {
     if (!lse)
         return fail(AAREN_ERR_INVALID_ARG, "lse is NULL (aaren_scan takes no lse)");
-    const int64_t s[3] = {H * N * d, N * d, d};
-    return scan_dense(q, k, v, o, lse, B, H, N, d, s, s, scale, in_dtype, out_dtype, workspace,
-                      workspace_bytes, hip_stream);
+    return scan_dense(q, k, v, o, lse, B, H, N, d, nullptr, nullptr, scale, in_dtype, out_dtype,
+                      workspace, workspace_bytes, hip_stream);
 }
 
 AAREN_API aaren_status aaren_scan_strided(const void *q, const void *k, const void *v, void *o,
@@ -642,8 +674,9 @@ namespace {
 
 aaren_status scan_packed(const void *q, const void *k, const void *v, void *o, float *lse,
                          const int64_t *offsets, int64_t num_seqs, int64_t total_tokens, int64_t H,
-                         int64_t d, float scale, aaren_dtype in_dtype, aaren_dtype out_dtype,
-                         void *workspace, size_t workspace_bytes, void *hip_stream)
+                         int64_t d, float scale, const aaren_dtype &in_dtype,
+                         const aaren_dtype &out_dtype, void *workspace, size_t workspace_bytes,
+                         void *hip_stream)
 {
     if (num_seqs < 0 || total_tokens < 0 || H < 0)
         return fail(AAREN_ERR_INVALID_ARG, "negative size (num_seqs %lld, T %lld, H %lld)",
@@ -866,7 +899,7 @@ AAREN_API aaren_status aaren_append(const void *q, const void *k, const void *v,
 
 AAREN_API size_t aaren_self_attention_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d)
 {
-    if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128))
+    if (B < 0 || H < 0 || N < 0 || N > aaren::kAttnMaxN || (d != 64 && d != 128))
         return 0;
     const int64_t elems = mul_checked({B, H, d, aaren::attn_padded_keys(N)});
     if (elems < 0)

@@ -13,6 +13,7 @@
 // the next layer as x.
 #include <rocblas/rocblas.h>
 
+#include <cstring>
 #include <mutex>
 #include <unordered_map>
 
@@ -71,7 +72,7 @@ const char *layer_init(int device)
         err = "warm-up product failed";
     if (hipStreamSynchronize(nullptr) != hipSuccess && !err)
         err = "warm-up product did not complete";
-    hipFree(buf);
+    (void)hipFree(buf);
     if (err) {
         rocblas_destroy_handle(h);
         return err;
@@ -102,7 +103,9 @@ AAREN_API aaren_status aaren_layer_forward(const void *x, const void *w_kv, cons
         return aaren_layer_fail(AAREN_ERR_INVALID_ARG, "negative size");
     if (d != 64 && d != 128)
         return aaren_layer_fail(AAREN_ERR_UNSUPPORTED, "supported head dimensions are 64 and 128");
-    if (out_dtype != AAREN_F32 && out_dtype != AAREN_BF16)
+    int out_code;  // read from the bytes: a C caller may pass any int
+    std::memcpy(&out_code, &out_dtype, sizeof out_code);
+    if (out_code != AAREN_F32 && out_code != AAREN_BF16)
         return aaren_layer_fail(AAREN_ERR_UNSUPPORTED, "unknown output dtype");
     const int64_t rows = B * N, cols = 2 * H * d;
     if (B * N == 0 || H == 0)
