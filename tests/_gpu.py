@@ -1,6 +1,7 @@
 """Helpers shared by the GPU parity tests."""
 from __future__ import annotations
 
+import math
 import sys
 
 import numpy as np
@@ -44,16 +45,16 @@ def scan_header_error(ws: torch.Tensor) -> int:
     return int(ws[12:16].view(torch.int32).item())
 
 
-# dq = scale * sum_i ds_i k_i adds B*N (or T) terms per head, in a fixed tree
-# of about 100 levels (8 rows per lane, 16 lane groups, the tiles' partials).
-# With rounding errors of independent signs the sum's error is about
-# sqrt(depth) 2^-24 times the root-sum-square of the terms, and the sum itself
-# is of that size for independent inputs: a scaled error of order 1e-6, as
-# measured. 1e-4 leaves two orders of magnitude of margin and is still far
-# below what losing one lane group's 8-row partial does at the dense
-# workload's shape (about 1e-2; test_gpu_workloads shows the check failing
-# on such a planted loss).
-DQ_TOL = 1e-4
+# dq = scale * sum_i ds_i k_i adds n = B*N (or T) terms per head. Rounding
+# errors of independent signs grow a sum's error like sqrt(n) 2^-24 times the
+# terms' size; the tolerance on the scaled error |dq - ref| / (1 + |ref|) is
+# 8 sqrt(n) 2^-24, and never below 1e-4. Measured at full size: the dense
+# batch (n = 131072, bound 1.7e-4) about 1e-6..4e-6, the packed batch
+# (n = 4,151,461, bound 9.8e-4) 1.0e-4. Losing one lane group's 8-row partial
+# at the dense shape moves dq by about 6e-3 of (1 + |dq|), which the check
+# catches (test_gpu_workloads plants it).
+def dq_tol(n_terms: int) -> float:
+    return max(1e-4, 8.0 * math.sqrt(n_terms) * 2.0 ** -24)
 
 
 def gpu_scaled_err(got: torch.Tensor, ref: np.ndarray) -> float:

@@ -11,11 +11,22 @@ import torch
 import exact_softmax_attention_02_amd as aaren
 import oracle
 import workloads
-from _gpu import (DQ_TOL, TOL, TOL_BF16_OUT, announce, check, dev, gpu_scaled_err, host32,
+from _gpu import (TOL, TOL_BF16_OUT, announce, check, dev, dq_tol, gpu_scaled_err, host32,
                   progress, scan_header_error)
 
 pytestmark = pytest.mark.gpu
 W = workloads.WORKLOADS
+
+
+def _dq_report(got, ref) -> str:
+    """Where dq's scaled error peaks: that error, the absolute error and the
+    reference there, and the largest |dq|."""
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    sc = err / (1 + np.abs(ref))
+    i = np.unravel_index(int(sc.argmax()), sc.shape)
+    return (f"dq worst scaled {sc[i]:.2e} (|err| {err[i]:.2e} at |dq| {abs(ref[i]):.2e}; "
+            f"max |dq| {np.abs(ref).max():.2e})")
 
 
 @pytest.fixture(autouse=True)
@@ -154,7 +165,8 @@ def test_dense_gradients_in_full(name):
     e_v = check(dv, rv, 1e-5, "dv")
     got_q = host32(dq).astype(np.float64)
     e_q = oracle.max_scaled_err(got_q, rq)
-    assert e_q <= DQ_TOL, f"dq: {e_q:.3e}"
+    tol_q = dq_tol(B * N)
+    assert e_q <= tol_q, f"dq: {e_q:.3e}"
     # The check would see one lane group's 8-row partial lost: remove rows
     # 8..15 of batch row 3's first tile from head h's sum (the terms
     # scale ds_i k_i, with scale ds_i = dk_ij / q_j along q's largest j).
@@ -164,8 +176,8 @@ def test_dense_gradients_in_full(name):
         lost = (rk[3, h, 8:16, j] / qh[h, j])[:, None] * kh[3, h, 8:16]
         planted = got_q.copy()
         planted[h] -= lost.sum(axis=0)
-        assert oracle.max_scaled_err(planted, rq) > DQ_TOL, h
-    print(f"{name} gradients: dq {e_q:.3e} dk {e_k:.3e} dv {e_v:.3e}")
+        assert oracle.max_scaled_err(planted, rq) > tol_q, h
+    print(f"{name} gradients: dq {e_q:.3e} dk {e_k:.3e} dv {e_v:.3e}; {_dq_report(got_q, rq)}")
 
 
 def test_stream_appends_in_full():
@@ -253,7 +265,7 @@ def test_layer_stack_in_full():
 def test_packed_gradients_in_full():
     """Gradients of the packed workload (1024 sequences, lengths U{1..8192},
     H=8, d=64) in full against the oracle, sequence by sequence; dq to
-    DQ_TOL."""
+    dq_tol(T)."""
     w = W["ragged_backward"]
     sz = w.sizes
     H, d = sz["H"], sz["d"]
@@ -276,8 +288,9 @@ def test_packed_gradients_in_full():
     e_v = check(dv, rv, 1e-5, "packed dv")
     del dv, rv
     e_q = oracle.max_scaled_err(host32(dq), rq)
-    assert e_q <= DQ_TOL, f"dq: {e_q:.3e}"
-    print(f"packed gradients: T={T} dq {e_q:.3e} dk {e_k:.3e} dv {e_v:.3e}")
+    print(f"packed gradients: T={T} dq {e_q:.3e} dk {e_k:.3e} dv {e_v:.3e}; "
+          f"{_dq_report(host32(dq), rq)}")
+    assert e_q <= dq_tol(T), f"dq: {e_q:.3e}"
 
 
 def test_mean_query_in_full():
