@@ -35,6 +35,7 @@ AAREN_F32, AAREN_BF16 = 0, 1
 EXPORTS = (
     "aaren_version", "aaren_status_string", "aaren_last_error", "aaren_workspace_clear",
     "aaren_init", "aaren_workspace_status", "aaren_scan_lse", "aaren_scan_segmented_lse",
+    "aaren_scan_noalloc",
     "aaren_scan_workspace_size", "aaren_scan", "aaren_scan_segmented_workspace_size",
     "aaren_scan_segmented", "aaren_state_init", "aaren_step", "aaren_reduce_workspace_size",
     "aaren_reduce", "aaren_scan_backward_workspace_size", "aaren_scan_backward", "aaren_append",
@@ -69,6 +70,7 @@ def _load():
         "aaren_scan_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_scan": (I, [P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
         "aaren_scan_lse": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
+        "aaren_scan_noalloc": (I, [P, P, P, P, I64, I64, I64, I64, F, I, I, P]),
         "aaren_scan_segmented_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_scan_segmented": (I, [P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ, P]),
         "aaren_scan_segmented_lse": (I, [P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P, SZ,
@@ -289,6 +291,27 @@ def aaren_scan(q, k, v, scale=None, out_dtype=None, out=None, workspace=None, ls
                                   wsb, _stream(dev)))
     _debug_check(ws, "aaren_scan")
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+@_on_tensor_device
+def aaren_scan_noalloc(q, k, v, scale=None, out_dtype=None, out=None):
+    """aaren_scan with the library's static per-GPU workspace (no workspace
+    argument, nothing allocated by the library; `out` may be given so that
+    nothing is allocated here either). Shapes needing more than 64 MiB of
+    scan workspace are rejected."""
+    dev = _need_cuda(q, k, v, out)
+    B, H, N, d = k.shape
+    if q.shape != (H, d) or v.shape != k.shape or q.dtype != k.dtype or v.dtype != k.dtype:
+        raise ValueError("expected q [H,d] and k, v [B,H,N,d] of one dtype")
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty(B, H, N, d, dtype=out_dtype, device=dev)
+    elif out.shape != k.shape or out.dtype != out_dtype:
+        raise ValueError("out must be [B,H,N,d] of out_dtype")
+    _check(lib.aaren_scan_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d,
+                                  default_scale(d) if scale is None else float(scale),
+                                  _dtype_code(k.dtype), _dtype_code(out_dtype), _stream(dev)))
+    return out
 
 
 def aaren_scan_lse(q, k, v, scale=None, out_dtype=None, out=None, workspace=None, lse=None):

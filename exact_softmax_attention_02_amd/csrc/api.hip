@@ -8,7 +8,6 @@
 #include <cstring>
 #include <mutex>
 #include <unordered_map>
-#include <unordered_set>
 
 #include "layout.h"
 #include "self_attention.h"
@@ -184,19 +183,23 @@ constexpr uint32_t kGroupInterleaved = 8;
 // captured call always records its counter clear in the graph, and a
 // workspace once used under capture is never taken as clean again: every
 // later call on it clears its counters first.
+struct WorkspaceRecord {
+    size_t clean = SIZE_MAX;  // counter bytes known to be zero (a new workspace: all)
+    bool captured = false;    // used under capture: never taken as clean again
+};
 std::mutex g_ws_mutex;
-std::unordered_map<const void *, size_t> g_ws_clean;
-std::unordered_set<const void *> g_ws_captured;
+std::unordered_map<const void *, WorkspaceRecord> g_ws;
 
-aaren_status prepare_counters(void *workspace, size_t need, bool captured, hipStream_t stream)
+// `own`: the record of a workspace the library keeps itself (the static
+// scratch of aaren_scan_noalloc), so that such calls look nothing up and
+// insert nothing; null for a caller's workspace.
+aaren_status prepare_counters(void *workspace, size_t need, bool captured, hipStream_t stream,
+                              WorkspaceRecord *own = nullptr)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if (captured)
-        g_ws_captured.insert(workspace);
-    auto it = g_ws_clean.find(workspace);
-    size_t clean = it == g_ws_clean.end() ? SIZE_MAX : it->second;
-    if (g_ws_captured.count(workspace))
-        clean = 0;
+    WorkspaceRecord &rec = own ? *own : g_ws[workspace];
+    rec.captured = rec.captured || captured;
+    const size_t clean = rec.captured ? 0 : rec.clean;
     if (need > clean) {
         aaren_status st = hip_status(
             aaren::launch_fill_zero(static_cast<uint8_t *>(workspace) + aaren::kHeaderBytes, need,
@@ -205,7 +208,39 @@ aaren_status prepare_counters(void *workspace, size_t need, bool captured, hipSt
         if (st != AAREN_OK)
             return st;
     }
-    g_ws_clean[workspace] = need;
+    rec.clean = need;
+    return AAREN_OK;
+}
+
+// ---- the static scan workspace of aaren_scan_noalloc ---------------------------
+// For callers that cannot allocate, the scan's workspace is a static device
+// array: one copy per GPU, held until the process ends, shared by every
+// aaren_scan_noalloc call on that GPU. On the host its name only stands in
+// for the symbol: kernels and fills get the address hipGetSymbolAddress gives
+// for the current device (g_scratch), never the name.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+void *g_scratch[kMaxDevices];                // guarded by g_ws_mutex
+WorkspaceRecord g_scratch_record[kMaxDevices];
+
+// Once per device, with it current: find the array's address and zero it (a
+// fill kernel, then a synchronisation: no call may see it before).
+aaren_status scratch_setup(int device, void **out)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return fail(AAREN_ERR_UNSUPPORTED, "device %d: at most %d devices", device, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (!g_scratch[device]) {
+        void *ptr = nullptr;
+        CHECK(hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)),
+                         "hipGetSymbolAddress of the scan scratch"));
+        CHECK(hip_status(aaren::launch_fill_zero(ptr, kScratchBytes, nullptr), "scratch clear"));
+        CHECK(hip_status(hipDeviceSynchronize(), "scratch clear"));
+        g_scratch_record[device] = WorkspaceRecord{};
+        g_scratch[device] = ptr;
+    }
+    *out = g_scratch[device];
     return AAREN_OK;
 }
 
@@ -248,6 +283,8 @@ AAREN_API aaren_status aaren_init(void)
 {
     int device = 0;
     CHECK(hip_status(hipGetDevice(&device), "hipGetDevice"));
+    void *ws = nullptr;
+    CHECK(scratch_setup(device, &ws));
     if (const char *err = aaren::layer_init(device))
         return fail(AAREN_ERR_HIP, "device %d: %s", device, err);
     return AAREN_OK;
@@ -263,7 +300,7 @@ AAREN_API aaren_status aaren_workspace_clear(void *workspace, size_t workspace_b
                                              static_cast<hipStream_t>(hip_stream)),
                      "workspace clear launch"));
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    g_ws_clean[workspace] = SIZE_MAX;
+    g_ws[workspace].clean = SIZE_MAX;
     return AAREN_OK;
 }
 
@@ -304,7 +341,7 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
                         int64_t B, int64_t H, int64_t N, int64_t d, const int64_t *kv_strides,
                         const int64_t *o_strides, float scale, const aaren_dtype &in_dtype,
                         const aaren_dtype &out_dtype, void *workspace, size_t workspace_bytes,
-                        void *hip_stream)
+                        void *hip_stream, WorkspaceRecord *own_record = nullptr)
 {
     if (B < 0 || H < 0 || N < 0)
         return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
@@ -390,7 +427,7 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
                 (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles, rows);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const bool cap = capturing(st);
-    CHECK(prepare_counters(workspace, counter_bytes(B * H), cap, st));
+    CHECK(prepare_counters(workspace, counter_bytes(B * H), cap, st, own_record));
     CHECK(call_epoch(p.header, cap, st, &p.epoch));
     return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, false, st),
                       "scan launch");
@@ -416,6 +453,47 @@ AAREN_API aaren_status aaren_scan_lse(const void *q, const void *k, const void *
         return fail(AAREN_ERR_INVALID_ARG, "lse is NULL (aaren_scan takes no lse)");
     return scan_dense(q, k, v, o, lse, B, H, N, d, nullptr, nullptr, scale, in_dtype, out_dtype,
                       workspace, workspace_bytes, hip_stream);
+}
+
+AAREN_API aaren_status aaren_scan_noalloc(const void *q, const void *k, const void *v, void *o,
+                                          int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                          aaren_dtype in_dtype, aaren_dtype out_dtype,
+                                          void *hip_stream)
+{
+    // what needs no device first: the workspace this shape needs must fit
+    if (B < 0 || H < 0 || N < 0)
+        return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
+                    (long long)B, (long long)H, (long long)N);
+    CHECK(check_common(d, in_dtype, out_dtype));
+    const int64_t elems = mul_checked({B, H, N, d});
+    if (elems < 0)
+        return fail(AAREN_ERR_UNSUPPORTED, "B*H*N*d overflows");
+    if (elems == 0)
+        return AAREN_OK;
+    const size_t need = aaren_scan_workspace_size(B, H, N, d);
+    if (need == 0 || need > kScratchBytes)
+        return fail(AAREN_ERR_UNSUPPORTED,
+                    "this shape needs %zu bytes of scan workspace; the static scratch holds %zu",
+                    need, kScratchBytes);
+    int device = 0;
+    CHECK(hip_status(hipGetDevice(&device), "hipGetDevice"));
+    if (device < 0 || device >= kMaxDevices)
+        return fail(AAREN_ERR_UNSUPPORTED, "device %d: at most %d devices", device, kMaxDevices);
+    void *ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_ws_mutex);
+        ws = g_scratch[device];
+    }
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (!ws) {
+        if (capturing(st))
+            return fail(AAREN_ERR_UNSUPPORTED,
+                        "the scan scratch of this device is not set up: call aaren_init (or "
+                        "aaren_scan_noalloc once) outside graph capture first");
+        CHECK(scratch_setup(device, &ws));
+    }
+    return scan_dense(q, k, v, o, nullptr, B, H, N, d, nullptr, nullptr, scale, in_dtype,
+                      out_dtype, ws, kScratchBytes, hip_stream, &g_scratch_record[device]);
 }
 
 AAREN_API aaren_status aaren_scan_strided(const void *q, const void *k, const void *v, void *o,

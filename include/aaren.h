@@ -109,7 +109,8 @@ const char *aaren_last_error(void);
 /* ---- set-up ------------------------------------------------------------------
  * Prepares the calling thread's current HIP device for the calls that keep
  * state in the library: creates the rocBLAS handle aaren_layer_forward runs
- * its projection with (rocBLAS allocates its workspace then). Call it once per
+ * its projection with (rocBLAS allocates its workspace then), and sets up the
+ * static scan workspace of aaren_scan_noalloc. Call it once per
  * device, before the first aaren_layer_forward there, and never while a stream
  * of the process is being captured into a graph (it allocates); further calls
  * on an initialised device do nothing. It is the only call that allocates.
@@ -181,6 +182,24 @@ aaren_status aaren_scan_lse(const void *q, const void *k, const void *v, void *o
                             int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                             aaren_dtype in_dtype, aaren_dtype out_dtype,
                             void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* aaren_scan for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same scan and
+ * output, with the workspace taken from a static array the library keeps on
+ * each GPU (64 MiB, held until the process ends) instead of a caller's
+ * buffer. The call allocates nothing. Shapes whose
+ * aaren_scan_workspace_size(B,H,N,d) exceeds 64 MiB are rejected with
+ * UNSUPPORTED (e.g. B*H*N up to about 14.9 million rows at d = 64 fit).
+ * The array is set up (its address resolved and zero-filled, with a device
+ * synchronisation) by aaren_init, or by the first aaren_scan_noalloc call on
+ * the device; if that first call is made under graph capture it returns
+ * UNSUPPORTED and enqueues nothing. Every call on a GPU shares that GPU's
+ * array: calls that can overlap in time on one GPU (different streams,
+ * threads) race and give unspecified results. Other statuses as for
+ * aaren_scan. */
+aaren_status aaren_scan_noalloc(const void *q, const void *k, const void *v, void *o,
+                                int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                aaren_dtype in_dtype, aaren_dtype out_dtype, void *hip_stream);
 
 /* ---- gradients of the dense many-to-many scan -------------------------------
  * "Attention as an RNN" (review, proposed method) presents the many-to-many

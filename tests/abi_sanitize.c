@@ -97,6 +97,12 @@ int main(void)
     EXPECT(aaren_scan_strided(A, A, A, A, NULL, 1, 8, 100, 64, huge3, st3, .125f, F, F, A, WS, NULL),
            AAREN_ERR_UNSUPPORTED);
 
+    EXPECT(aaren_scan_noalloc(A, A, A, A, 1, 1, (int64_t)1 << 27, 64, .125f, F, F, NULL),
+           AAREN_ERR_UNSUPPORTED);
+    EXPECT(aaren_scan_noalloc(A, A, A, A, BIG, BIG, BIG, 64, .125f, F, F, NULL),
+           AAREN_ERR_UNSUPPORTED);
+    EXPECT(aaren_scan_noalloc(A, A, A, A, 1, 1, 16, 64, .125f, BAD, F, NULL), AAREN_ERR_UNSUPPORTED);
+
     /* packed scan */
     EXPECT(aaren_scan_segmented(A, A, A, A, NULL, 2, 10, 1, 64, .125f, F, F, A, WS, NULL),
            AAREN_ERR_INVALID_ARG);

@@ -271,3 +271,15 @@ def test_header_is_plain_c99(tmp_path):
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
                         "-I", os.path.dirname(HEADER), str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_noalloc_scan_validation():
+    na = lambda **kw: L.aaren_scan_noalloc(kw.get("q", A), A, A, A, kw.get("B", 1), 1,
+                                           kw.get("N", 16), kw.get("d", 64), 0.125,
+                                           kw.get("ind", 0), 0, None)
+    assert na(B=-1) == S["arg"]
+    assert na(d=96) == S["unsup"]
+    assert na(ind=5) == S["unsup"]
+    assert na(N=0) == S["ok"]                  # nothing to do
+    assert na(N=1 << 27) == S["unsup"]         # beyond the static scratch
+    assert "static scratch" in aaren.aaren_last_error()
