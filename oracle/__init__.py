@@ -52,6 +52,7 @@ def _configure(lib):
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_scan.argtypes = [f32p, f32p, f32p, i64, i64, i64, i64, ctypes.c_double,
                                 f64p, opt64, opt64]
+    lib.oracle_scan_f64.argtypes = [f64p, f64p, f64p, i64, i64, i64, i64, ctypes.c_double, f64p]
     lib.oracle_scan_segmented.argtypes = [f32p, f32p, f32p, i64p, i64, i64, i64, i64,
                                           ctypes.c_double, f64p, opt64, opt64]
     lib.oracle_step.argtypes = [f32p, f32p, f32p, f64p, f64p, f64p, opt64,
@@ -62,8 +63,8 @@ def _configure(lib):
                                          ctypes.c_double, f64p, f64p, f64p]
     lib.oracle_self_attention.argtypes = [f32p, f32p, f32p, i64, i64, i64, i64, ctypes.c_double,
                                           ctypes.c_int, i64, i64, f64p, opt64]
-    for fn in (lib.oracle_scan, lib.oracle_scan_segmented, lib.oracle_step, lib.oracle_reduce,
-               lib.oracle_scan_backward):
+    for fn in (lib.oracle_scan, lib.oracle_scan_f64, lib.oracle_scan_segmented, lib.oracle_step,
+               lib.oracle_reduce, lib.oracle_scan_backward):
         fn.restype = ctypes.c_int
     return lib
 
@@ -109,6 +110,19 @@ def scan(q, k, v, scale, stats: bool = False):
     if rc:
         raise ValueError("oracle_scan rejected its arguments")
     return (o, m, lse) if stats else o
+
+
+def scan_f64(q, k, v, scale):
+    """The many-to-many output for float64 inputs (keys and values that are
+    not float32 values, such as the layer's projections): q [H,d], k, v
+    [B,H,N,d] -> o [B,H,N,d] float64, the same recurrence as scan()."""
+    q, k, v = (np.ascontiguousarray(np.asarray(a, np.float64)) for a in (q, k, v))
+    B, H, N, d = k.shape
+    assert q.shape == (H, d) and v.shape == k.shape
+    o = np.empty((B, H, N, d), np.float64)
+    if _load().oracle_scan_f64(q, k, v, B, H, N, d, float(scale), o):
+        raise ValueError("oracle_scan_f64 rejected its arguments")
+    return o
 
 
 def scan_segmented(q, k, v, offsets, scale, stats: bool = False):
@@ -234,17 +248,20 @@ def self_attention(q, k, v, scale, causal: bool = True, rows=None, stats: bool =
 
 def mean_query_attention(hq, k, v, scale, stats: bool = False):
     """Global-aggregation attention of the pooling network on the
-    efficient-transformer page (PoNet, "Global aggregation"): per (b,h) the
-    query g is the mean of hq over the N tokens (float64, then float32: every
-    query here is float32), and o is the attention of g over all N pairs
-    (the reduction). hq, k, v [B,H,N,d] -> o [B,H,d] (and g [B,H,d])."""
+    efficient-transformer page (PoNet, "Global aggregation" and its two
+    equations): per (b,h) the query g is the mean of hq over the N tokens,
+    and o is the attention of g over all N pairs: the softmax of the scores
+    scale <g, k_n> weighting the values. Everything in float64 (g is not
+    rounded). hq, k, v [B,H,N,d] -> o [B,H,d] (and g [B,H,d] float64)."""
     hq, k, v = _f32(hq), _f32(k), _f32(v)
     B, H, N, d = k.shape
-    g = hq.astype(np.float64).mean(axis=2).astype(np.float32)
+    g = hq.astype(np.float64).mean(axis=2)
     o = np.empty((B, H, d), np.float64)
     for b in range(B):
         for h in range(H):
-            o[b, h] = reduce(g[b, h][None], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], scale)[0, 0]
+            s = float(scale) * (k[b, h].astype(np.float64) @ g[b, h])
+            p = np.exp(s - s.max())
+            o[b, h] = (p @ v[b, h].astype(np.float64)) / p.sum()
     return (o, g) if stats else o
 
 
@@ -258,18 +275,18 @@ def bf16_round(a):
 
 def layer_forward(x, w_kv, q, scale, out_bf16: bool = True):
     """One Aaren layer: x [B,N,Dm], w_kv [Dm, 2*H*d] (W_K | W_V), q [H,d]
-    -> o [B,N,H,d] float64. [K | V] = x w_kv in float64, stored as float32
-    (the layer keeps K and V in fp32), then the many-to-many scan of q_h over
-    each (b, h) ("Attention as an RNN" review, proposed method: a learned
-    query, the prefix-scan output); with out_bf16 the output is rounded to
-    bfloat16, the precision a stacked layer receives."""
+    -> o [B,N,H,d] float64. [K | V] = x w_kv in float64, then the
+    many-to-many scan of q_h over each (b, h) in float64 ("Attention as an
+    RNN" review, proposed method: a learned query, the prefix-scan output);
+    with out_bf16 the output is rounded to bfloat16, the precision a stacked
+    layer receives."""
     x, w_kv, q = (np.asarray(t, np.float64) for t in (x, w_kv, q))
     B, N, Dm = x.shape
     H, d = q.shape
-    kv = (x.reshape(B * N, Dm) @ w_kv).reshape(B, N, 2, H, d).astype(np.float32)
+    kv = (x.reshape(B * N, Dm) @ w_kv).reshape(B, N, 2, H, d)
     k = np.ascontiguousarray(kv[:, :, 0].transpose(0, 2, 1, 3))   # [B,H,N,d]
     v = np.ascontiguousarray(kv[:, :, 1].transpose(0, 2, 1, 3))
-    o = scan(q.astype(np.float32), k, v, scale).transpose(0, 2, 1, 3)  # [B,N,H,d]
+    o = scan_f64(q, k, v, scale).transpose(0, 2, 1, 3)  # [B,N,H,d]
     return bf16_round(o) if out_bf16 else np.ascontiguousarray(o)
 
 

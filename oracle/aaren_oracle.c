@@ -151,6 +151,52 @@ int oracle_scan(const float *q, const float *k, const float *v,
     return 0;
 }
 
+/* The same many-to-many scan for inputs that are not float32 values (keys
+ * and values computed in double, e.g. a projection of the inputs): q [H,d],
+ * k, v [B,H,N,d] and o in double. Each pair is absorbed as above: the state
+ * is rescaled by e^{m_old - s} when the score s is a new maximum, otherwise
+ * the pair enters with weight e^{s - m}; o is w / u after every pair. */
+int oracle_scan_f64(const double *q, const double *k, const double *v,
+                    int64_t B, int64_t H, int64_t N, int64_t d, double scale, double *o)
+{
+    if (B < 0 || H < 0 || N < 0 || d < 1)
+        return 1;
+    int64_t units = B * H;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc((size_t)d * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t unit = 0; unit < units; ++unit) {
+            const double *qh = q + (unit % H) * d;
+            double m = -INFINITY, u = 0.0;
+            memset(w, 0, (size_t)d * sizeof(double));
+            for (int64_t i = 0; i < N; ++i) {
+                const double *kr = k + (unit * N + i) * d, *vr = v + (unit * N + i) * d;
+                double dot = 0.0;
+                for (int64_t j = 0; j < d; ++j)
+                    dot += qh[j] * kr[j];
+                const double sc = scale * dot;
+                if (sc > m) {
+                    const double shrink = (m == -INFINITY) ? 0.0 : exp(m - sc);
+                    u = u * shrink + 1.0;
+                    for (int64_t j = 0; j < d; ++j)
+                        w[j] = w[j] * shrink + vr[j];
+                    m = sc;
+                } else {
+                    const double p = exp(sc - m);
+                    u += p;
+                    for (int64_t j = 0; j < d; ++j)
+                        w[j] += p * vr[j];
+                }
+                for (int64_t j = 0; j < d; ++j)
+                    o[(unit * N + i) * d + j] = w[j] / u;
+            }
+        }
+        free(w);
+    }
+    return 0;
+}
+
 /* Many-to-many scan over a packed variable-length batch: each sequence is
  * scanned on its own. q [H,d]; k, v, o [T,H,d] token-major; offsets [S+1]
  * with offsets[0] = 0, non-decreasing, offsets[S] = T. */

@@ -325,10 +325,26 @@ def check_bf16_round(orc, seed=27):
     assert np.array_equal(orc.bf16_round(r), ref)
 
 
+def check_scan_f64(orc, seed=30):
+    """The float64-input scan: against brute force on keys and values that
+    are not float32 values (a spread of ±200 in the scores included), and
+    equal to the float32-input scan where the inputs are float32 values."""
+    rng = _rng(seed)
+    B, H, N, d = 2, 3, 37, 5
+    q = rng.standard_normal((H, d))
+    k = rng.standard_normal((B, H, N, d)) * (1 + np.arange(N)[:, None] * 2.0)
+    v = rng.standard_normal((B, H, N, d)) / 3.0
+    o = orc.scan_f64(q, k, v, 0.7)
+    _close(o, brute.brute_scan_batch(q, k, v, 0.7), 1e-12, "float64 scan vs brute force")
+    q32, k32, v32 = (a.astype(np.float32) for a in (q, k, v))
+    _close(orc.scan_f64(q32.astype(np.float64), k32.astype(np.float64), v32.astype(np.float64), 0.7),
+           orc.scan(q32, k32, v32, 0.7), 1e-14, "float64 scan == float32-input scan")
+
+
 def check_layer(orc, seed=28):
     """The layer is the projection followed by the scan: per (b, h), brute
     force over k = x W_K[:, h], v = x W_V[:, h] (written out here with its own
-    indexing), the output rounded to bf16 or not."""
+    indexing, in float64), the output rounded to bf16 or not."""
     rng = _rng(seed)
     B, N, Dm, H, d = 2, 9, 5, 3, 4
     x = rng.standard_normal((B, N, Dm)).astype(np.float32)
@@ -341,7 +357,7 @@ def check_layer(orc, seed=28):
         for h in range(H):
             kh = np.einsum("nm,mj->nj", x[b].astype(np.float64), w[:, h * d:(h + 1) * d])
             vh = np.einsum("nm,mj->nj", x[b].astype(np.float64), w[:, (H + h) * d:(H + h + 1) * d])
-            ref = brute.brute_scan(q[h], kh.astype(np.float32), vh.astype(np.float32), scale)
+            ref = brute.brute_scan(q[h], kh, vh, scale)
             _close(o[b, :, h], ref, 1e-12, "layer vs projection + brute scan")
     ob = orc.layer_forward(x, w, q, scale, out_bf16=True)
     assert np.array_equal(ob, orc.bf16_round(o))
@@ -357,11 +373,11 @@ def check_mean_query(orc, seed=29):
     hq, k, v = (rng.standard_normal((B, H, N, d)).astype(np.float32) for _ in range(3))
     scale = 0.6
     o, g = orc.mean_query_attention(hq, k, v, scale, stats=True)
-    gt = torch.from_numpy(hq).double().mean(dim=2).float().double()
+    gt = torch.from_numpy(hq).double().mean(dim=2)
     w = torch.softmax(scale * torch.einsum("bhnd,bhd->bhn", torch.from_numpy(k).double(), gt), dim=-1)
     ref = torch.einsum("bhn,bhnd->bhd", w, torch.from_numpy(v).double()).numpy()
     _close(o, ref, 1e-12, "mean query vs torch")
-    assert np.allclose(g, gt.float().numpy(), rtol=2.0 ** -23, atol=0)
+    assert np.allclose(g, gt.numpy(), rtol=1e-15, atol=0)
     qh = rng.standard_normal((H, d)).astype(np.float32)
     same = np.ascontiguousarray(np.broadcast_to(qh[None, :, None, :], (B, H, N, d)))
     _close(orc.mean_query_attention(same, k, v, scale), orc.reduce(qh, k, v, scale), 1e-13,
@@ -501,5 +517,5 @@ def check_backward_closed_forms(orc, seed=24):
 
 ALL = [check_golden, check_scan_vs_definition, check_stats, check_single_token,
        check_running_mean, check_two_tokens, check_dominating_key, check_shift_invariance,
-       check_convex_hull, check_bracketing, check_reduce, check_step, check_append, check_self_attention, check_bf16_round, check_layer, check_mean_query, check_segmented,
+       check_convex_hull, check_bracketing, check_reduce, check_step, check_append, check_self_attention, check_bf16_round, check_scan_f64, check_layer, check_mean_query, check_segmented,
        check_backward, check_segmented_backward, check_backward_finite_differences, check_backward_closed_forms]

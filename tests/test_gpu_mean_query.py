@@ -23,7 +23,7 @@ def test_mean_query_matches_oracle(B, H, N, d, dt):
     scale = workloads.default_scale(d)
     o, gq = aaren.aaren_mean_query_attention(hq, k, v, scale, return_query=True)
     ref, rg = oracle.mean_query_attention(host32(hq), host32(k), host32(v), scale, stats=True)
-    # the float64 sums may round to float32 one ulp apart
+    # the GPU's g is the float64 mean rounded once to float32: within half an ulp
     assert np.allclose(host32(gq), rg, rtol=2.0 ** -23, atol=0)
     err = check(o, ref, TOL[torch_dt], "mean query")
     print(f"mean query {B}x{H}x{N}x{d} {dt}: {err:.2e}")

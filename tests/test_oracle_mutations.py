@@ -38,6 +38,12 @@ MUTATIONS = [
      "                else emit(m, u, w, d, o + row * d, m_out ? m_out + row : NULL,\n"
      "                     lse_out ? lse_out + row : NULL);\n"
      "                absorb(&m, &u, w, d, score(qh, k + row * d, d, scale), v + row * d);"),
+    ("float64 scan: rescale exponent sign flipped", "oracle_scan_f64", "exp(m - sc)",
+     "exp(sc - m)"),
+    ("float64 scan: value sum not rescaled", "oracle_scan_f64",
+     "w[j] = w[j] * shrink + vr[j];", "w[j] = w[j] + vr[j];"),
+    ("float64 scan: query of head 0 for all heads", "oracle_scan_f64",
+     "const double *qh = q + (unit % H) * d;", "const double *qh = q;"),
     ("segmented: query of head 0 for all heads", "oracle_scan_segmented",
      "score(q + h * d, k + row * d", "score(q, k + row * d"),
     ("segmented: head stride dropped", "oracle_scan_segmented",
