@@ -9,6 +9,9 @@ already resident in HBM:
   ragged                   : one aaren_scan_segmented call (token-heads = H*T)
   stream                   : aaren_state_init + 256 aaren_step calls
                                                            (token-heads = S*H*256)
+  stream_hbm               : the same 256 calls over 8 state sets in turn, so
+                             each call reads its state from HBM (the single
+                             set stays mostly in the Infinity Cache)
   append                   : aaren_state_init + 16 aaren_append calls of 16
                              tokens, the same 256 tokens per stream
   backward                 : one aaren_scan_backward call on the dense batch
@@ -169,7 +172,7 @@ def make(name: str, device):
     b = Workload()
     b.name = name
     if name != "copy":
-        w = wl.WORKLOADS["dense" if name == "backward" else name]
+        w = wl.WORKLOADS[{"backward": "dense", "stream_hbm": "stream"}.get(name, name)]
         z = w.sizes
         b.describe = w.describe()
         b.dtype = {"f32": "f32", "bf16": "bf16->f32"}[w.dtype]
@@ -379,7 +382,13 @@ def make(name: str, device):
         q, k, v = wl.step_inputs(S, H, d, T, w.seed, device=device)
         b.inputs = dict(q=q, k=k, v=v)
         scale = wl.default_scale(d)
-        m, u, st_w = aaren.new_state(S, H, d, device=device)
+        # stream_hbm: the same calls over 8 state sets in turn (each set takes
+        # every 8th token), so that a call's state was last touched 7 calls
+        # (about 9.5 GB of traffic) earlier and comes from HBM, not from the
+        # 256 MB Infinity Cache the single state set mostly stays in
+        nstate = 8 if name == "stream_hbm" else 1
+        states = [aaren.new_state(S, H, d, device=device) for _ in range(nstate)]
+        m, u, st_w = states[0]
         o = torch.empty(S, H, d, device=device)
 
         # events every T/8 appends (the last step's are kept): the time per
@@ -389,11 +398,13 @@ def make(name: str, device):
         stream_ = torch.cuda.current_stream(device)
 
         def step():
-            aaren.aaren_state_init(m, u, st_w)
+            for sm, su, sw in states:
+                aaren.aaren_state_init(sm, su, sw)
             for t in range(T):
                 if t % seg == 0:
                     marks[t // seg].record(stream_)
-                aaren.aaren_step(q, k[t], v[t], m, u, st_w, scale, o_t=o)
+                sm, su, sw = states[t % nstate]
+                aaren.aaren_step(q, k[t], v[t], sm, su, sw, scale, o_t=o)
             if T % seg == 0:
                 marks[-1].record(stream_)
 
@@ -410,7 +421,12 @@ def make(name: str, device):
         # m, u read and written (16 B)
         b.bytes_per_launch = S * H * (5 * d * 4 + 4 * 4)
         b.config = {"workload": f"RNN step, {T} appends per stream {b.describe}", "S": S, "H": H,
-                    "d": d, "appends": T, "in_dtype": "f32", "out_dtype": "f32"}
+                    "d": d, "appends": T, "in_dtype": "f32", "out_dtype": "f32",
+                    "state_sets": nstate}
+        if nstate > 1:
+            b.config["workload"] = (f"RNN step, {T} calls over {nstate} state sets in turn "
+                                    f"({T // nstate} appends each; state read from HBM) "
+                                    f"{b.describe}")
         b.kernel = "step_kernel"
 
         def cpu(budget_s):
@@ -637,7 +653,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
                     choices=["single", "dense", "long_bf16", "ragged", "stream", "append",
-                             "reduce", "backward", "backward_bf16", "ragged_backward",
+                             "stream_hbm", "reduce", "backward", "backward_bf16",
+                             "ragged_backward",
                              "self_attn", "layer",
                              "mean_query", "copy"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
