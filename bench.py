@@ -6,6 +6,7 @@
 One step is one pass of the hot path over one batch of the workload, inputs
 already resident in HBM:
   dense, single, long_bf16 : one aaren_scan call          (token-heads = B*H*N)
+  dense_share              : the dense batch's share of one GPU out of 8 (B=4)
   ragged                   : one aaren_scan_segmented call (token-heads = H*T)
   stream                   : aaren_state_init + 256 aaren_step calls
                                                            (token-heads = S*H*256)
@@ -652,7 +653,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense",
-                    choices=["single", "dense", "long_bf16", "ragged", "stream", "append",
+                    choices=["single", "dense", "dense_share", "long_bf16", "ragged", "stream",
+                             "append",
                              "stream_hbm", "reduce", "backward", "backward_bf16",
                              "ragged_backward",
                              "self_attn", "layer",

@@ -57,6 +57,8 @@ WORKLOADS = {
     "single": Workload("single", "dense", dict(B=1, H=1, N=1024, d=64), "f32", 1),
     # the dense batch the headline throughput is quoted on
     "dense": Workload("dense", "dense", dict(B=32, H=8, N=4096, d=64), "f32", 2),
+    # one GPU's share of the dense batch split over 8 GPUs by batch row
+    "dense_share": Workload("dense_share", "dense", dict(B=4, H=8, N=4096, d=64), "f32", 2),
     # long sequences, bf16 inputs, scores stretched to +-80
     "long_bf16": Workload("long_bf16", "dense", dict(B=4, H=16, N=65536, d=128), "bf16", 3,
                           score_span=80.0),
