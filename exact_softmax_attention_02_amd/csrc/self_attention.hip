@@ -192,8 +192,29 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
     constexpr int KS = D / 16;          // 16-wide k-steps of S^T = K Q^T
     constexpr int DT = D / 32;          // 32-row tiles of O^T
     constexpr int KC = D / (8 * kAttnWaves);  // 1 KB copies per wave per tile (K and V^T each)
-    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kAttnKeys * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sv[2][D * kAttnKeys];
+    // Two buffers per operand, each its own array: the tile copies below write
+    // LDS asynchronously (counted by vmcnt), and the compiler makes a read of
+    // LDS wait for every copy that may land in the same array. With the
+    // buffers apart and the buffer index a compile-time constant (d = 128),
+    // reading tile j no longer waits for tile j+1's copies.
+    __shared__ __attribute__((aligned(16))) uint16_t sk0[kAttnKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sk1[kAttnKeys * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sv0[D * kAttnKeys];
+    __shared__ __attribute__((aligned(16))) uint16_t sv1[D * kAttnKeys];
+    // a buffer index is a compile-time constant (std::integral_constant) or,
+    // on the d = 64 path, an int
+    auto skb = [&](auto b) -> uint16_t * {
+        if constexpr (std::is_integral_v<decltype(b)>) return b ? sk1 : sk0;
+        else if constexpr (decltype(b)::value == 0) return sk0;
+        else return sk1;
+    };
+    auto svb = [&](auto b) -> uint16_t * {
+        if constexpr (std::is_integral_v<decltype(b)>) return b ? sv1 : sv0;
+        else if constexpr (decltype(b)::value == 0) return sv0;
+        else return sv1;
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h32 = lane >> 5, l32 = lane & 31;
@@ -252,7 +273,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
     const int vr0 = wv * 8 + lane / 8;
     const uint32_t voff = (uint32_t)(vr0 * 2 * p.Np + 16 * ((lane % 8) ^ vswz(vr0)));
     const uint32_t vstep = (uint32_t)(64 * p.Np);  // 32 V^T rows, in bytes
-    auto load_tile = [&](int j, int buf) {
+    auto load_tile = [&](int j, auto buf) {
         const int64_t k0 = (int64_t)j * kAttnKeys;
         const int64_t kbytes = (p.N - k0) * 2 * D;
 #pragma unroll
@@ -260,18 +281,18 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
             const int64_t left = kbytes - 4096 * c;
             const auto kr = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(kh + k0 * D + 2048 * c), (short)0, (int)(left > 0 ? left : 0), kBufferWord3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lptr)(&sk[buf][(kAttnWaves * c + wv) * 512]),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lptr)(skb(buf) + (kAttnWaves * c + wv) * 512),
                                                      16, koff, 0, 0, 0);
         }
         const auto vr = __builtin_amdgcn_make_buffer_rsrc((void *)(vth + k0), (short)0,
                                                           (int)((D * p.Np - k0) * 2), kBufferWord3);
 #pragma unroll
         for (int c = 0; c < KC; ++c)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lptr)(&sv[buf][(kAttnWaves * c + wv) * 512]),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lptr)(svb(buf) + (kAttnWaves * c + wv) * 512),
                                                      16, voff, vstep * c, 0, 0);
     };
 
-    load_tile(0, 0);
+    load_tile(0, B0{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -290,10 +311,10 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
     // this workgroup (causal); keys at offset >= lim from the tile's first key
     // are then masked for this lane's query (excluded from the maximum, weight
     // exactly 0).
-    auto tile = [&](int buf, int lim, auto edge_tag) {
+    auto tile = [&](auto buf, int lim, auto edge_tag) {
         constexpr bool EDGE = decltype(edge_tag)::value;
         auto kfrag = [&](int t, int kk) {
-            return load16(&sk[buf][(32 * t + krow) * D + 8 * ((2 * kk + h32) ^ kswz(32 * t + krow))]);
+            return load16(skb(buf) + (32 * t + krow) * D + 8 * ((2 * kk + h32) ^ kswz(32 * t + krow)));
         };
         f32x16 s[2] = {f32x16{}, f32x16{}};
         if constexpr (D == 128) {
@@ -366,8 +387,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     const int vr = 32 * dt + l32;
-                    const u32x4 a = load16(&sv[buf][vr * kAttnKeys +
-                                                    8 * ((4 * t + 2 * s2 + h32) ^ vswz(vr))]);
+                    const u32x4 a = load16(svb(buf) + vr * kAttnKeys +
+                                                    8 * ((4 * t + 2 * s2 + h32) ^ vswz(vr)));
                     oacc[dt] = mfma32h(a, ph, oacc[dt]);
                 }
             }
@@ -379,20 +400,19 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
     int64_t nfull = p.N / kAttnKeys;
     if (p.causal && (q0 + 1) / kAttnKeys < nfull)
         nfull = (q0 + 1) / kAttnKeys;
-    int j = 0;
-    for (; j < (int)nfull; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < ntiles)
-            load_tile(j + 1, buf ^ 1);  // that buffer was last read before the previous barrier
+    // d = 128: the loops go two tiles per trip, so that every buffer index is
+    // a constant
+    auto full = [&](int jj, auto buf, auto other) {
+        if (jj + 1 < ntiles)
+            load_tile(jj + 1, other);  // that buffer was last read before the previous barrier
         tile(buf, kAttnKeys, std::integral_constant<bool, false>{});
         __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
         __syncthreads();
-    }
-    for (; j < ntiles; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < ntiles)
-            load_tile(j + 1, buf ^ 1);
-        const int64_t k0 = (int64_t)j * kAttnKeys;
+    };
+    auto edge = [&](int jj, auto buf, auto other) {
+        if (jj + 1 < ntiles)
+            load_tile(jj + 1, other);
+        const int64_t k0 = (int64_t)jj * kAttnKeys;
         int64_t lim = p.N - k0;
         if (p.causal && qi + 1 - k0 < lim)
             lim = qi + 1 - k0;
@@ -400,6 +420,33 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
              std::integral_constant<bool, true>{});
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    int j = 0;
+    if constexpr (D == 64) {
+        // held to 128 VGPRs: one loop body, the buffer chosen at run time
+        for (; j < (int)nfull; ++j)
+            full(j, j & 1, (j & 1) ^ 1);
+        for (; j < ntiles; ++j)
+            edge(j, j & 1, (j & 1) ^ 1);
+    } else {
+        for (; j + 1 < (int)nfull; j += 2) {
+            full(j, B0{}, B1{});
+            full(j + 1, B1{}, B0{});
+        }
+        if (j < (int)nfull) {
+            full(j, B0{}, B1{});
+            ++j;
+        }
+        // tile j is in buffer j & 1
+        if ((j & 1) && j < ntiles) {
+            edge(j, B1{}, B0{});
+            ++j;
+        }
+        for (; j < ntiles; j += 2) {
+            edge(j, B0{}, B1{});
+            if (j + 1 < ntiles)
+                edge(j + 1, B1{}, B0{});
+        }
     }
 
     lsum += __shfl_xor(lsum, 32);
