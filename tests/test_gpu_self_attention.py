@@ -23,7 +23,8 @@ def inputs(B, H, N, d, seed, spread=1.0):
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 @pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 64), (1, 2, 63, 64), (2, 2, 129, 64),
                                      (1, 1, 200, 128), (2, 3, 300, 128), (1, 2, 1000, 64),
-                                     (1, 1, 1100, 128), (1, 1, 192, 128), (3, 3, 385, 128)])
+                                     (1, 1, 1100, 128), (1, 1, 192, 128), (3, 3, 385, 128),
+                                     (1, 1, 50, 128), (2, 1, 64, 128), (1, 2, 330, 128)])
 def test_self_attention_matches_oracle(B, H, N, d, causal):
     announce(f"self-attention B={B} H={H} N={N} d={d} causal={causal}")
     q, k, v = inputs(B, H, N, d, seed=N + d)
