@@ -13,9 +13,11 @@ namespace aaren {
 
 // Tile shapes: a workgroup of kAttnWaves waves takes 32 queries per wave; keys
 // and values go through LDS 64 at a time, double buffered (64 KB at d = 128,
-// 32 KB at d = 64). d = 128 runs 2 waves per SIMD (up to 256 VGPRs); d = 64 is held
-// to 128 VGPRs, so four workgroups per CU make 4.
-constexpr int kAttnWaves = 4;
+// 32 KB at d = 64). d = 128 runs 2 waves per SIMD (up to 256 VGPRs), one
+// workgroup per CU, which halves the tile copies per flop against 4-wave
+// workgroups; d = 64 is held to 128 VGPRs, so two workgroups per CU make 4
+// waves per SIMD.
+constexpr int kAttnWaves = 8;
 constexpr int kAttnQueries = 32 * kAttnWaves;
 constexpr int kAttnKeys = 64;
 // heads whose query tiles are interleaved in the launch order

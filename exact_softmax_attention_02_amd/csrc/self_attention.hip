@@ -258,38 +258,49 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
     constexpr int KRPI = 1024 / (2 * D);  // K rows per 1 KB copy
     const uint16_t *kh = p.k + bh * p.N * D;
     const uint16_t *vth = p.vt + bh * D * p.Np;
-    // Copy c of a wave fills 1 KB block kAttnWaves * c + wave of the tile: the
-    // rows of its copy 0 plus 16c (K, d = 128), 32c (K, d = 64) or 32c (V^T).
-    // Both swizzles depend on a row modulo 16 only, so every copy of a lane
-    // uses copy 0's byte offset (one VGPR per operand); the rest is scalar: a
-    // K copy has its own buffer starting c * 4 KB further, whose record count
-    // ends at the head's last key (rows past N read as zeros, masked later),
-    // and a V^T copy adds c * 32 rows as the scalar offset (V^T reads never
-    // leave the head's padded rows). Offsets and counts stay below 2^31 for
-    // N <= kAttnMaxN.
+    // Copy c of a wave fills 1 KB block kAttnWaves * c + wave of the tile, the
+    // rows of its copy 0 plus 4 * kAttnWaves * c (K, d = 128) or
+    // 8 * kAttnWaves * c (V^T); d = 64 takes one copy per operand. Both
+    // swizzles depend on a row modulo 16 only, so every copy of a lane uses
+    // copy 0's byte offset (one VGPR per operand); the rest is scalar. V^T and
+    // every K tile that ends at or before N go through one buffer per head,
+    // the tile's start and the copy's step as the scalar offset; neither
+    // leaves that buffer (V^T reads stay in the head's padded rows). The last
+    // K tile, which may pass N, gives each copy a buffer of its own whose
+    // record count ends at the head's last key, so rows past N read as zeros
+    // (masked later). Offsets and counts stay below 2^31 for N <= kAttnMaxN.
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int kr0 = wv * KRPI + lane / (D / 8);
     const uint32_t koff = (uint32_t)(kr0 * 2 * D + 16 * ((lane % (D / 8)) ^ kswz(kr0)));
     const int vr0 = wv * 8 + lane / 8;
     const uint32_t voff = (uint32_t)(vr0 * 2 * p.Np + 16 * ((lane % 8) ^ vswz(vr0)));
-    const uint32_t vstep = (uint32_t)(64 * p.Np);  // 32 V^T rows, in bytes
+    const uint32_t vstep = (uint32_t)(16 * kAttnWaves * p.Np);  // 8 * kAttnWaves V^T rows, in bytes
+    // one descriptor per head for K (tiles that end at or before N) and V^T
+    const auto khr = __builtin_amdgcn_make_buffer_rsrc((void *)kh, (short)0, (int)(p.N * 2 * D), kBufferWord3);
+    const auto vtr = __builtin_amdgcn_make_buffer_rsrc((void *)vth, (short)0, (int)(D * p.Np * 2), kBufferWord3);
     auto load_tile = [&](int j, auto buf) {
         const int64_t k0 = (int64_t)j * kAttnKeys;
-        const int64_t kbytes = (p.N - k0) * 2 * D;
+        if (k0 + kAttnKeys <= p.N) {
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            const int64_t left = kbytes - 4096 * c;
-            const auto kr = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(kh + k0 * D + 2048 * c), (short)0, (int)(left > 0 ? left : 0), kBufferWord3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lptr)(skb(buf) + (kAttnWaves * c + wv) * 512),
-                                                     16, koff, 0, 0, 0);
+            for (int c = 0; c < KC; ++c)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(khr, (lptr)(skb(buf) + (kAttnWaves * c + wv) * 512), 16,
+                                                         koff, (int)(k0 * 2 * D) + 1024 * kAttnWaves * c, 0, 0);
+        } else {
+            // the last tile: each copy's record count ends at the head's last key
+            const int64_t kbytes = (p.N - k0) * 2 * D;
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const int64_t left = kbytes - 1024 * kAttnWaves * c;
+                const auto kr = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(kh + k0 * D + 512 * kAttnWaves * c), (short)0, (int)(left > 0 ? left : 0), kBufferWord3);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lptr)(skb(buf) + (kAttnWaves * c + wv) * 512),
+                                                         16, koff, 0, 0, 0);
+            }
         }
-        const auto vr = __builtin_amdgcn_make_buffer_rsrc((void *)(vth + k0), (short)0,
-                                                          (int)((D * p.Np - k0) * 2), kBufferWord3);
 #pragma unroll
         for (int c = 0; c < KC; ++c)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lptr)(svb(buf) + (kAttnWaves * c + wv) * 512),
-                                                     16, voff, vstep * c, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vtr, (lptr)(svb(buf) + (kAttnWaves * c + wv) * 512), 16,
+                                                     voff, (int)(2 * k0) + (int)(vstep * c), 0, 0);
     };
 
     load_tile(0, B0{});
@@ -400,8 +411,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, D == 64 ? 4 : 2) void self_attenti
     int64_t nfull = p.N / kAttnKeys;
     if (p.causal && (q0 + 1) / kAttnKeys < nfull)
         nfull = (q0 + 1) / kAttnKeys;
-    // d = 128: the loops go two tiles per trip, so that every buffer index is
-    // a constant
+    // the loops go two tiles per trip, so that every buffer index is a constant
     auto full = [&](int jj, auto buf, auto other) {
         if (jj + 1 < ntiles)
             load_tile(jj + 1, other);  // that buffer was last read before the previous barrier
