@@ -148,25 +148,31 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
         }
     }
 
+    // Every input load is unconditional: a row at or past N reads the
+    // stream's last row instead (always in bounds), and its leaf exponent is
+    // -inf, so it weighs exactly 0 in pass 1 and pass 2 skips it. A load
+    // inside a branch would make the compiler wait at the end of the branch
+    // for it and for every load issued before it.
+    auto clamp_row = [&](int r) { return row0 + r < p.N ? row0 + r : p.N - 1; };
+    const int64_t sbase = bat * p.batch_stride + head * p.head_stride;
+    auto row_at = [&](int r) { return sbase + clamp_row(r) * rs; };
+
     // dO and O first: the tile's aggregate needs only them and L, so it is
     // published (and the look-back chain moves on) before K and V arrive
     RawCols<Tin> gr[R];
     u32x4 orr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        gr[r] = RawCols<Tin>{};
-        orr[r] = u32x4{0, 0, 0, 0};
-        if (r < nvalid) {
-            gr[r] = load_cols<Tin, true>(pg + base + r * rs, gl);
-            orr[r] = load_cols<float, true>(p.o + base + r * rs, gl);
-        }
+        gr[r] = load_cols<Tin, true>(pg + row_at(r), gl);
+        orr[r] = load_cols<float, true>(p.o + row_at(r), gl);
     }
     float lm[R];  // leaf exponent -L_r, log2 units
-    const float *lse_row = p.lse + bat * p.lse_batch_stride + head * p.lse_head_stride +
-                           row0 * p.lse_row_stride;
+    const float *lse_s = p.lse + bat * p.lse_batch_stride + head * p.lse_head_stride;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        lm[r] = (r < nvalid) ? -lse_row[r * p.lse_row_stride] * kLog2e : kNegInf;
+    for (int r = 0; r < R; ++r) {
+        const float l = lse_s[clamp_row(r) * p.lse_row_stride];
+        lm[r] = (r < nvalid) ? -l * kLog2e : kNegInf;
+    }
 
     // delta_r = <g_r, o_r>
     float dl[R];
@@ -216,15 +222,11 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
     // K and V land during the barrier and the look-back (O's registers are free)
     RawCols<Tin> kr[R], vr[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        kr[r] = vr[r] = RawCols<Tin>{};
-        if (r < nvalid)
-            kr[r] = load_cols<Tin, true>(pk + base + r * rs, gl);
-    }
+    for (int r = 0; r < R; ++r)
+        kr[r] = load_cols<Tin, true>(pk + row_at(r), gl);
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        if (r < nvalid)
-            vr[r] = load_cols<Tin, true>(pv + base + r * rs, gl);
+        vr[r] = load_cols<Tin, true>(pv + row_at(r), gl);
     __syncthreads();
 
     // fold a group state G onto X (the rows after it): G (+) X, or G alone if
