@@ -570,7 +570,7 @@ def make(name: str, device):
         b.inputs = dict(x=x, w_kv=ws_, q=qs)
         scale = wl.default_scale(d)
         bufs = [torch.empty(B, N, H, d, dtype=torch.bfloat16, device=device) for _ in range(2)]
-        work = torch.zeros(aaren.aaren_layer_workspace_size(B, N, H, d), dtype=torch.uint8,
+        work = torch.zeros(aaren.aaren_layer_workspace_size(B, N, max(Dm, H * d), H, d), dtype=torch.uint8,
                            device=device)
 
         def step():
@@ -582,16 +582,19 @@ def make(name: str, device):
         b.kind = "layer"
         b.unit = "tokens/s"
         b.bound = "mfma"
-        # projection flops per layer (2 per multiply-add) plus the scan's 4d per token-head
-        b.flops_per_launch = sum(2 * B * N * (Dm if l == 0 else H * d) * 2 * H * d + 4 * d * B * N * H
-                                 for l in range(L))
+        # Flops of the folded layer (2 per multiply-add): the product's V columns
+        # and one score column per head (u_h = W_K^h q_h; its three-part split
+        # and the zero column are not counted), plus the scan's 2d per
+        # token-head for the weighted sum of V. K = x W_K is never formed.
+        b.flops_per_launch = sum(2 * B * N * (Dm if l == 0 else H * d) * (H * d + H) +
+                                 2 * d * B * N * H for l in range(L))
         b.units = B * N
         b.bytes_per_launch = 0
         b.config = {"workload": f"{L} stacked Aaren layers {b.describe}", "B": B, "N": N,
                     "Dm": Dm, "H": H, "d": d, "layers": L, "in_dtype": "bf16",
                     "out_dtype": "bf16", "flops_per_step": b.flops_per_launch}
-        b.kernel = "rocBLAS projection GEMMs + scan_kernel (the whole stack)"
-        b.dispatches_per_launch = L  # one GEMM and one scan per layer
+        b.kernel = "layer_fold_kernel + rocBLAS projection GEMMs + scan_kernel (the whole stack)"
+        b.dispatches_per_launch = L  # traffic counters are read per layer (fold, GEMM, scan)
 
         def cpu(budget_s):
             import oracle

@@ -80,7 +80,7 @@ def _load():
         "aaren_append": (I, [P, P, P, P, P, P, P, I64, I64, I64, I64, F, I, I, P]),
         "aaren_self_attention_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_scan_strided": (I, [P, P, P, P, P, I64, I64, I64, I64, P, P, F, I, I, P, SZ, P]),
-        "aaren_layer_workspace_size": (SZ, [I64, I64, I64, I64]),
+        "aaren_layer_workspace_size": (SZ, [I64, I64, I64, I64, I64]),
         "aaren_mean_query_attention_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_scan_segmented_backward_workspace_size": (SZ, [I64, I64, I64, I64]),
         "aaren_scan_segmented_backward": (I, [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, F,
@@ -501,8 +501,8 @@ def aaren_scan_strided(q, k, v, scale=None, out_dtype=None, out=None, workspace=
     return (out, lse) if (return_lse or lse is not None) else out
 
 
-def aaren_layer_workspace_size(B, N, H, d) -> int:
-    return int(lib.aaren_layer_workspace_size(B, N, H, d))
+def aaren_layer_workspace_size(B, N, Dm, H, d) -> int:
+    return int(lib.aaren_layer_workspace_size(B, N, Dm, H, d))
 
 
 @_on_tensor_device
@@ -520,7 +520,7 @@ def aaren_layer_forward(x, w_kv, q, scale=None, out_dtype=None, out=None, worksp
     if out is None:
         out = torch.empty(B, N, H, d, dtype=out_dtype, device=dev)
     aaren_init(dev)  # once per device: the projection's rocBLAS handle
-    need = aaren_layer_workspace_size(B, N, H, d)
+    need = aaren_layer_workspace_size(B, N, Dm, H, d)
     ws = workspace if workspace is not None else _workspace("layer", need, dev, True)
     _check(lib.aaren_layer_forward(_ptr(x), _ptr(w_kv), _ptr(q), _ptr(out), B, N, Dm, H, d,
                                    default_scale(d) if scale is None else float(scale),

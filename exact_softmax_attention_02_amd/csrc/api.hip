@@ -341,7 +341,8 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
                         int64_t B, int64_t H, int64_t N, int64_t d, const int64_t *kv_strides,
                         const int64_t *o_strides, float scale, const aaren_dtype &in_dtype,
                         const aaren_dtype &out_dtype, void *workspace, size_t workspace_bytes,
-                        void *hip_stream, WorkspaceRecord *own_record = nullptr)
+                        void *hip_stream, WorkspaceRecord *own_record = nullptr,
+                        const float *scores = nullptr, int64_t s_head_stride = 0)
 {
     if (B < 0 || H < 0 || N < 0)
         return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
@@ -378,6 +379,15 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
     CHECK(check_ptr(o, "o"));
     if (reinterpret_cast<uintptr_t>(lse) & 3u)
         return fail(AAREN_ERR_ALIGNMENT, "lse is not 4-byte aligned");
+    if (scores) {  // 4 floats per row and head, addressed like k but for the head stride
+        if (in_dtype != AAREN_F32)
+            return fail(AAREN_ERR_UNSUPPORTED, "precomputed scores go with float32 values");
+        CHECK(check_ptr(scores, "scores"));
+        if (s_head_stride < 0 || s_head_stride % 4 ||
+            mul_checked({H - 1, s_head_stride, 4}) < 0 ||
+            mul_checked({H - 1, s_head_stride, 4}) > (int64_t(1) << 62) - kv_end)
+            return fail(AAREN_ERR_INVALID_ARG, "score head stride");
+    }
     const int rows = aaren::scan_rows_per_tile((int)d, in_dtype);
     const int64_t chunks = ceil_div(N, rows);
     const int64_t tiles = B * H * chunks;
@@ -418,6 +428,8 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
     p.num_tiles = (uint32_t)tiles;
     p.stress = stress_enabled();
     p.qscale = scale * 1.44269504088896340736f;
+    p.scores = scores;
+    p.s_head_stride = s_head_stride;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     p.header = reinterpret_cast<uint32_t *>(ws);
     p.counters = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes);
@@ -507,6 +519,20 @@ AAREN_API aaren_status aaren_scan_strided(const void *q, const void *k, const vo
         return fail(AAREN_ERR_INVALID_ARG, "strides are NULL");
     return scan_dense(q, k, v, o, lse, B, H, N, d, kv_strides, o_strides, scale, in_dtype,
                       out_dtype, workspace, workspace_bytes, hip_stream);
+}
+
+aaren_status aaren::scan_scored_strided(const float *scores, int64_t s_head_stride, const float *v,
+                                        void *o, int64_t B, int64_t H, int64_t N, int64_t d,
+                                        const int64_t *v_strides, const int64_t *o_strides,
+                                        aaren_dtype out_dtype, void *workspace,
+                                        size_t workspace_bytes, void *hip_stream)
+{
+    if (!scores || !v_strides || !o_strides)
+        return fail(AAREN_ERR_INVALID_ARG, "scores or strides are NULL");
+    // q and k are not read: the scores stand in for both
+    return scan_dense(scores, scores, v, o, nullptr, B, H, N, d, v_strides, o_strides, 1.f,
+                      AAREN_F32, out_dtype, workspace, workspace_bytes, hip_stream, nullptr, scores,
+                      s_head_stride);
 }
 
 // ---- backward of the dense scan -----------------------------------------------

@@ -87,6 +87,11 @@ struct ScanParams {
     // (k and v share one set, o has its own)
     int64_t batch_stride, head_stride, row_stride;
     int64_t o_batch_stride, o_head_stride, o_row_stride;
+    // Scores given instead of keys (k unused): row r of stream s holds 4
+    // floats at b * batch_stride + h * s_head_stride + r * row_stride, whose
+    // first three sum to the score in log2 units (scale * log2(e) included).
+    const float *scores;
+    int64_t s_head_stride;
     int64_t chunks;          // tiles per stream
     uint32_t group;          // consecutive workgroups that serve one stream
     uint32_t chunks_padded;  // chunks rounded up to a multiple of group
@@ -179,6 +184,15 @@ struct BackwardParams {
 // Launchers (each validates nothing: the API layer did).
 hipError_t launch_scan(const ScanParams &p, int D, aaren_dtype in, aaren_dtype out, bool segmented,
                        hipStream_t stream);
+
+// The dense scan of fp32 values with precomputed scores (the layer's path,
+// api.hip): scores[b, n, h] is 4 floats at b*v_strides[0] + h*s_head_stride +
+// n*v_strides[2] whose first three sum to scale * log2(e) * <q_h, k_n>.
+aaren_status scan_scored_strided(const float *scores, int64_t s_head_stride, const float *v,
+                                 void *o, int64_t B, int64_t H, int64_t N, int64_t d,
+                                 const int64_t *v_strides, const int64_t *o_strides,
+                                 aaren_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                                 void *hip_stream);
 hipError_t launch_segment_flags(const int64_t *offsets, int64_t num_seqs, int64_t total_tokens,
                                 uint32_t *bitmap, int64_t words, hipStream_t stream);
 int scan_rows_per_tile(int D, aaren_dtype in);

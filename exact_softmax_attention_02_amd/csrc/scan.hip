@@ -33,6 +33,8 @@
 //    and the look-back stops at an aggregate that holds a start (segmented
 //    scan with head flags).
 // Exponentials are base 2: q is pre-multiplied by scale*log2(e).
+#include <type_traits>
+
 #include "lookback.h"
 
 namespace aaren {
@@ -51,7 +53,9 @@ struct ScanShape {
     static_assert(D % 64 == 0, "d = 64 or 128");
 };
 
-template <int D, typename Tin, typename Tout, int R, int WAVES, bool SEG>
+// SCORED: the scores come precomputed (p.scores, see ScanParams) and K is not
+// read; dense fp32 values only.
+template <int D, typename Tin, typename Tout, int R, int WAVES, bool SEG, bool SCORED>
 __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
 {
     using S = ScanShape<D, Tin, R, WAVES>;
@@ -111,13 +115,20 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     const int64_t base = bat * p.batch_stride + head * p.head_stride + row0 * p.row_stride;  // column 0
     const Tin *kp = static_cast<const Tin *>(p.k) + base;
     const Tin *vp = static_cast<const Tin *>(p.v) + base;
-    u32x4 kr[R], vr[R];
+    u32x4 kr[R], vr[R];  // SCORED: kr[r] holds row r's score parts
+    const float *sp = nullptr;
+    if constexpr (SCORED)
+        sp = p.scores + bat * p.batch_stride + head * p.s_head_stride + row0 * p.row_stride;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         kr[r] = u32x4{0, 0, 0, 0};
         vr[r] = u32x4{0, 0, 0, 0};
-        if (r < nvalid)
-            kr[r] = load_slice<D, Tin, true>(kp + r * p.row_stride, gl);
+        if (r < nvalid) {
+            if constexpr (SCORED)
+                kr[r] = load16_stream(sp + r * p.row_stride);
+            else
+                kr[r] = load_slice<D, Tin, true>(kp + r * p.row_stride, gl);
+        }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)  // keys first: the scores need them first
@@ -140,24 +151,33 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
         }
     }
 
-    float qv[E];
-    widen<Tin>(load_slice<D, Tin, false>(static_cast<const Tin *>(p.q) + (stream % p.H) * D, gl), qv);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-        qv[e] *= p.qscale;
-
     // ---- scores (log2 units) ---------------------------------------------------
     float s[R];
+    if constexpr (SCORED) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        float kf[E];
-        widen<Tin>(kr[r], kf);
-        float part = 0.f;
+        for (int r = 0; r < R; ++r) {
+            const float sc = (__uint_as_float(kr[r][0]) + __uint_as_float(kr[r][1])) +
+                             __uint_as_float(kr[r][2]);
+            s[r] = (r < nvalid) ? sc : kNegInf;
+        }
+    } else {
+        float qv[E];
+        widen<Tin>(load_slice<D, Tin, false>(static_cast<const Tin *>(p.q) + (stream % p.H) * D, gl),
+                   qv);
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            part = __builtin_fmaf(qv[e], kf[e], part);
-        s[r] = group_sum<L>(part);
-        s[r] = (r < nvalid) ? s[r] : kNegInf;
+            qv[e] *= p.qscale;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float kf[E];
+            widen<Tin>(kr[r], kf);
+            float part = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                part = __builtin_fmaf(qv[e], kf[e], part);
+            s[r] = group_sum<L>(part);
+            s[r] = (r < nvalid) ? s[r] : kNegInf;
+        }
     }
 
     // ---- pass 1: the group's state (from its last sequence start, if any) ------
@@ -382,13 +402,14 @@ __global__ __launch_bounds__(256) void segment_flags_kernel(const int64_t *offse
     bitmap[i] = bits;
 }
 
-template <int D, typename Tin, typename Tout, bool SEG>
+template <int D, typename Tin, typename Tout, bool SEG, bool SCORED = false>
 static hipError_t launch_one(const ScanParams &p, hipStream_t stream)
 {
     constexpr int R = 16, WAVES = 4;
     static_assert(ScanShape<D, Tin, R, WAVES>::ROWS == scan_tile_rows(D, sizeof(Tin)),
                   "tile rows disagree with the workspace sizing");
-    hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, SEG>),
+    static_assert(!SCORED || (std::is_same_v<Tin, float> && !SEG), "scored: dense fp32 values");
+    hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, SEG, SCORED>),
                        dim3((unsigned)(p.streams * p.chunks_padded)),
                        dim3(64 * WAVES), 0, stream, p);
     return hipGetLastError();
@@ -410,6 +431,13 @@ static hipError_t dispatch_dtypes(const ScanParams &p, aaren_dtype in, aaren_dty
 hipError_t launch_scan(const ScanParams &p, int D, aaren_dtype in, aaren_dtype out, bool segmented,
                        hipStream_t stream)
 {
+    if (p.scores) {  // dense fp32 values (the caller checks)
+        if (D == 64)
+            return out == AAREN_F32 ? launch_one<64, float, float, false, true>(p, stream)
+                                    : launch_one<64, float, bf16, false, true>(p, stream);
+        return out == AAREN_F32 ? launch_one<128, float, float, false, true>(p, stream)
+                                : launch_one<128, float, bf16, false, true>(p, stream);
+    }
     if (D == 64)
         return segmented ? dispatch_dtypes<64, true>(p, in, out, stream)
                          : dispatch_dtypes<64, false>(p, in, out, stream);

@@ -349,19 +349,24 @@ aaren_status aaren_reduce(const void *q, const void *k, const void *v, void *o,
  * many-to-many output is the prefix scan; layers are stacked like
  * Transformer attention. Here (the pages print no layer formula; this is
  * the plainest reading):
- *   [K | V] = x [W_K | W_V]   (bf16 x, bf16 weights, fp32 products: rocBLAS)
+ *   K = x W_K, V = x W_V   (bf16 x, bf16 weights, fp32 products)
  *   o[b,n,h,:] = attention of q_h over K[b,0..n,h,:], V[b,0..n,h,:]
+ * The attention needs K only through the scores <q_h, k_n> = x_n (W_K^h q_h):
+ * the call folds q into W_K (u_h = W_K^h q_h, kept to fp32 precision as three
+ * bf16 parts), so one rocBLAS GEMM gives V and the scores and K is never
+ * formed; the result equals the definition's up to fp32 rounding.
  * x [B,N,Dm] bf16; w_kv [Dm, 2*H*d] bf16 row-major (columns 0..H*d-1 = W_K,
  * the rest W_V, head h in columns h*d..h*d+d-1 of each); q [H,d] float32;
  * o [B,N,H,d] (out_dtype; a stacked layer takes o, bf16, as its x with
- * Dm = H*d). The workspace (aaren_layer_workspace_size) holds K|V in fp32
+ * Dm = H*d). The workspace (aaren_layer_workspace_size, which needs Dm for
+ * the folded weights) holds those weights (bf16), V and the scores (fp32)
  * and the scan's state; zero-fill it once before first use, as for
- * aaren_scan. The projection runs through the rocBLAS handle aaren_init
- * created for the device; without it the call returns UNSUPPORTED and
- * enqueues nothing. It allocates nothing.
+ * aaren_scan; 0 means the sizes overflow. The projection runs through the
+ * rocBLAS handle aaren_init created for the device; without it the call
+ * returns UNSUPPORTED and enqueues nothing. It allocates nothing.
  * B*N*H = 0: OK, nothing done. Dm = 0 with rows: INVALID_ARG. Sizes beyond
  * the 32-bit GEMM interface: UNSUPPORTED. A GEMM failure: HIP. */
-size_t aaren_layer_workspace_size(int64_t B, int64_t N, int64_t H, int64_t d);
+size_t aaren_layer_workspace_size(int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t d);
 aaren_status aaren_layer_forward(const void *x, const void *w_kv, const float *q, void *o,
                                  int64_t B, int64_t N, int64_t Dm, int64_t H, int64_t d,
                                  float scale, aaren_dtype out_dtype, void *workspace,

@@ -67,7 +67,8 @@ int main(void)
                 (void)aaren_reduce_workspace_size(1, x, y, d);
                 (void)aaren_self_attention_workspace_size(x, 1, y, d);
                 (void)aaren_mean_query_attention_workspace_size(x, 1, y, d);
-                (void)aaren_layer_workspace_size(x, y, 8, d);
+                (void)aaren_layer_workspace_size(x, y, 64, 8, d);
+                (void)aaren_layer_workspace_size(1, x, y, 8, d);
                 ++cases;
             }
 

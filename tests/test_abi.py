@@ -207,9 +207,15 @@ def test_layer_validation():
     assert lf(x=A + 2) == S["align"]
     assert lf(wsb=64) == S["ws"]
     assert L.aaren_layer_forward(0, 0, 0, 0, 0, 10, 32, 2, 64, 0.125, 1, 0, 0, None) == 0
-    # [scan state][K|V in fp32]
-    assert aaren.aaren_layer_workspace_size(2, 100, 3, 64) == \
-        aaren.aaren_scan_workspace_size(2, 3, 100, 64) + 2 * 100 * 2 * 3 * 64 * 4
+    # [scan state][V and 4 score floats per head, padded to 128 columns, fp32]
+    # [folded weights, bf16, the same columns], each part rounded up to 256 bytes
+    r256 = lambda b: (b + 255) // 256 * 256
+    cols = (3 * 64 + 4 * 3 + 127) // 128 * 128
+    assert aaren.aaren_layer_workspace_size(2, 100, 96, 3, 64) == \
+        r256(aaren.aaren_scan_workspace_size(2, 3, 100, 64)) + r256(2 * 100 * cols * 4) + \
+        r256(96 * cols * 2)
+    assert aaren.aaren_layer_workspace_size(2, 100, -1, 3, 64) == 0
+    assert aaren.aaren_layer_workspace_size(1 << 40, 1 << 20, 96, 3, 64) == 0
 
 
 def test_mean_query_validation():

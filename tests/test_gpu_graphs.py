@@ -245,7 +245,7 @@ def test_layer_in_a_graph():
     B, N, Dm, H, d = 2, 1500, 256, 4, 64
     x, w, q = workloads.layer_inputs(B, N, Dm, H, d, 1, 41, device=dev())
     w, q = w[0], q[0]
-    wsp = torch.zeros(aaren.aaren_layer_workspace_size(B, N, H, d), dtype=torch.uint8, device=dev())
+    wsp = torch.zeros(aaren.aaren_layer_workspace_size(B, N, Dm, H, d), dtype=torch.uint8, device=dev())
     o = torch.empty(B, N, H, d, dtype=torch.bfloat16, device=dev())
     aaren.aaren_layer_forward(x, w, q, out=o, workspace=wsp)
     torch.cuda.synchronize()
@@ -269,7 +269,7 @@ import ctypes, torch, exact_softmax_attention_02_amd as aaren, workloads
 dev = torch.device("cuda:0")
 x, w, q = workloads.layer_inputs(1, 300, 128, 2, 64, 1, 43, device=dev)
 w, q = w[0], q[0]
-wsp = torch.zeros(aaren.aaren_layer_workspace_size(1, 300, 2, 64), dtype=torch.uint8, device=dev)
+wsp = torch.zeros(aaren.aaren_layer_workspace_size(1, 300, 128, 2, 64), dtype=torch.uint8, device=dev)
 o = torch.full((1, 300, 2, 64), 7.0, dtype=torch.bfloat16, device=dev)
 P = lambda t: ctypes.c_void_p(t.data_ptr())
 st = aaren.lib.aaren_layer_forward(P(x), P(w), P(q), P(o), 1, 300, 128, 2, 64, 0.125,

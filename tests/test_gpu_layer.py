@@ -48,7 +48,7 @@ def test_layer_matches_oracle(B, N, Dm, H, d):
     announce(f"layer B={B} N={N} Dm={Dm} H={H} d={d}")
     x, w, q = _layer_inputs(B, N, Dm, H, d, seed=N + Dm)
     scale = workloads.default_scale(d)
-    ws = torch.zeros(aaren.aaren_layer_workspace_size(B, N, H, d), dtype=torch.uint8, device=dev())
+    ws = torch.zeros(aaren.aaren_layer_workspace_size(B, N, Dm, H, d), dtype=torch.uint8, device=dev())
     o32 = aaren.aaren_layer_forward(x, w, q, scale, out_dtype=torch.float32, workspace=ws)
     o16 = aaren.aaren_layer_forward(x, w, q, scale, workspace=ws)
     torch.cuda.synchronize()
