@@ -61,6 +61,30 @@ def test_layer_matches_oracle(B, N, Dm, H, d):
     print(f"layer {B}x{N}x{Dm} H={H} d={d}: fp32 {e32:.2e} bf16 {e16:.2e}")
 
 
+@pytest.mark.parametrize("spread", [60.0])
+def test_layer_with_stretched_scores(spread):
+    """q scaled so that the largest |score| is `spread`: the scores reach the
+    scan as x (W_K q), with W_K q carried into the product as three bf16
+    parts. With all three the scores are off by the fp32 rounding of two dot
+    products (length Dm in the product, d in W_K q), so the bound scales with
+    the spread: 8 |s| (sqrt(Dm) + sqrt(d)) 2^-24. W_K q rounded to bf16 once
+    would move the scores by about |s| 2^-9 (0.1 here), far past it; two
+    parts (about |s| 2^-17) would stay inside this bound."""
+    announce(f"layer stretched scores {spread}")
+    B, N, Dm, H, d = 1, 800, 256, 2, 64
+    x, w, q = _layer_inputs(B, N, Dm, H, d, seed=77)
+    scale = workloads.default_scale(d)
+    xh, wh, qh = (host32(t).astype(np.float64) for t in (x, w, q))
+    kh = (xh @ wh[:, :H * d]).reshape(B, N, H, d)
+    s = scale * np.einsum("bnhd,hd->bnh", kh, qh)
+    q = q * float(spread / np.abs(s).max())
+    o32 = aaren.aaren_layer_forward(x, w, q, scale, out_dtype=torch.float32)
+    ref = oracle.layer_forward(host32(x), host32(w), host32(q), scale, out_bf16=False)
+    bound = max(1e-5, 8 * spread * (Dm ** 0.5 + d ** 0.5) * 2.0 ** -24)
+    err = check(o32, ref, bound, "layer stretched scores")
+    print(f"layer stretched scores {spread}: fp32 {err:.2e} (bound {bound:.1e})")
+
+
 def test_two_stacked_layers():
     """The second layer takes the first one's bf16 output (rounded on both
     sides: that rounding is part of the stack's definition). Where the GPU's
