@@ -32,6 +32,9 @@
 //  * Packed batches: a bitmap marks sequence starts; a start resets the state,
 //    and the look-back stops at an aggregate that holds a start (segmented
 //    scan with head flags).
+//  * Scored (the layer's form): the scores arrive precomputed, three fp32
+//    parts per row and head, and take the place of K's row and the dot
+//    product; the rest is unchanged.
 // Exponentials are base 2: q is pre-multiplied by scale*log2(e).
 #include <type_traits>
 
