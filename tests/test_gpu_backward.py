@@ -64,10 +64,15 @@ def test_backward_reproducible_and_empty():
     g = torch.randn_like(k)
     o, lse = aaren.aaren_scan(q, k, v, return_lse=True)
     first = aaren.aaren_scan_backward(q, k, v, o, g, lse)
+    ws = torch.zeros(aaren.aaren_scan_backward_workspace_size(B, H, N, d), dtype=torch.uint8,
+                     device=dev())
     for _ in range(5):
-        again = aaren.aaren_scan_backward(q, k, v, o, g, lse)
+        again = aaren.aaren_scan_backward(q, k, v, o, g, lse, workspace=ws)
         torch.cuda.synchronize()
         assert all(torch.equal(a, b) for a, b in zip(first, again))
+        # every stream's ticket counter is back at 0 after the call
+        counters = ws[256:256 + B * H * 128].view(torch.int32)
+        assert int(counters.abs().sum().item()) == 0
     # no rows: dq is zero
     z = torch.zeros(2, 0, 64, device=dev()).reshape(1, 2, 0, 64)
     dq = torch.full((2, 64), 7.0, device=dev())
