@@ -403,23 +403,32 @@ __attribute__((amdgpu_waves_per_eu(3))) void scan_backward_kernel(const Backward
 
 // dq[h] = sum of the B*chunks partials of head h, in a fixed order: thread
 // (sub, c4) adds rows sub, sub + SUB, ... of columns 4c4..4c4+3, then the SUB
-// subtotals are added in order.
+// subtotals are added in order. With stride > 1 it adds the rows 0, stride,
+// 2 stride, ... that scan_backward_dq_slice_kernel left.
 constexpr int kDqThreads = 1024;
+// Heads with more partials than this (packed batches: one per 128 tokens of
+// the whole batch) are summed in two levels, kDqSlice partials per workgroup
+// first, so that more than one workgroup per head reads them.
+constexpr int64_t kDqTwoLevel = 4096;
+constexpr int64_t kDqSlice = 256;
+constexpr int kDqSliceThreads = 256;
 
 template <int D>
-__global__ __launch_bounds__(kDqThreads) void scan_backward_dq_kernel(const BackwardParams p)
+__global__ __launch_bounds__(kDqThreads) void scan_backward_dq_kernel(const BackwardParams p,
+                                                                      int64_t stride)
 {
     constexpr int V4 = D / 4, SUB = kDqThreads / V4;
     __shared__ __attribute__((aligned(16))) float sh[SUB][D];
     const int tid = threadIdx.x, c4 = tid % V4, sub = tid / V4;
     const int64_t h = blockIdx.x;
     const int64_t count = (p.streams / p.H) * p.chunks;  // partials of this head
+    const int64_t rows = (count + stride - 1) / stride;
     const float *src = p.dq_partial + (size_t)h * count * D + 4 * c4;
     float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-    for (int64_t i = sub; i < count; i += SUB) {
+    for (int64_t i = sub; i < rows; i += SUB) {
         float x[4];
-        widen<float>(load16(src + (size_t)i * D), x);
+        widen<float>(load16(src + (size_t)(i * stride) * D), x);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             a[e] += x[e];
@@ -437,6 +446,40 @@ __global__ __launch_bounds__(kDqThreads) void scan_backward_dq_kernel(const Back
     }
 }
 
+// First level: workgroup (g, h) adds partials g*kDqSlice .. (g+1)*kDqSlice - 1
+// of head h in the same fixed order and writes the sum over the slice's first
+// partial (only this workgroup touches the slice).
+template <int D>
+__global__ __launch_bounds__(kDqSliceThreads) void scan_backward_dq_slice_kernel(
+    const BackwardParams p)
+{
+    constexpr int V4 = D / 4, SUB = kDqSliceThreads / V4;
+    __shared__ __attribute__((aligned(16))) float sh[SUB][D];
+    const int tid = threadIdx.x, c4 = tid % V4, sub = tid / V4;
+    const int64_t h = blockIdx.y, g = blockIdx.x;
+    const int64_t count = (p.streams / p.H) * p.chunks;
+    const int64_t first = g * kDqSlice, end = first + kDqSlice < count ? first + kDqSlice : count;
+    float *base = p.dq_partial + (size_t)h * count * D;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i = first + sub; i < end; i += SUB) {
+        float x[4];
+        widen<float>(load16(base + (size_t)i * D + 4 * c4), x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            a[e] += x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        sh[sub][4 * c4 + e] = a[e];
+    __syncthreads();  // every read of the slice is done before its first row is written
+    if (tid < D) {
+        float r = 0.f;
+        for (int s = 0; s < SUB; ++s)
+            r += sh[s][tid];
+        base[(size_t)first * D + tid] = r;
+    }
+}
+
 template <int D, typename Tin>
 static hipError_t backward_one(const BackwardParams &p, bool segmented, hipStream_t stream)
 {
@@ -451,8 +494,19 @@ static hipError_t backward_one(const BackwardParams &p, bool segmented, hipStrea
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
+    const int64_t count = (p.streams / p.H) * p.chunks;
+    int64_t stride = 1;
+    if (count > kDqTwoLevel) {
+        hipLaunchKernelGGL((scan_backward_dq_slice_kernel<D>),
+                           dim3((unsigned)((count + kDqSlice - 1) / kDqSlice), (unsigned)p.H),
+                           dim3(kDqSliceThreads), 0, stream, p);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        stride = kDqSlice;
+    }
     hipLaunchKernelGGL((scan_backward_dq_kernel<D>), dim3((unsigned)p.H), dim3(kDqThreads), 0,
-                       stream, p);
+                       stream, p, stride);
     return hipGetLastError();
 }
 
