@@ -342,7 +342,8 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
                         const int64_t *o_strides, float scale, const aaren_dtype &in_dtype,
                         const aaren_dtype &out_dtype, void *workspace, size_t workspace_bytes,
                         void *hip_stream, WorkspaceRecord *own_record = nullptr,
-                        const float *scores = nullptr, int64_t s_head_stride = 0)
+                        const float *scores = nullptr, int64_t s_head_stride = 0,
+                        bool check_only = false)
 {
     if (B < 0 || H < 0 || N < 0)
         return fail(AAREN_ERR_INVALID_ARG, "negative size (B %lld, H %lld, N %lld)",
@@ -402,6 +403,8 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
                     need);
     if (!aligned16(workspace))
         return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+    if (check_only)
+        return AAREN_OK;
 
     aaren::ScanParams p{};
     p.q = q;
@@ -534,6 +537,23 @@ aaren_status aaren::scan_scored_strided(const float *scores, int64_t s_head_stri
                       AAREN_F32, out_dtype, workspace, workspace_bytes, hip_stream, nullptr, scores,
                       s_head_stride);
 }
+
+// The checks of scan_scored_strided alone: its status for these arguments,
+// with nothing enqueued (the layer runs it before its own launches).
+namespace aaren {
+aaren_status scan_scored_check(const float *scores, int64_t s_head_stride, const float *v,
+                               void *o, int64_t B, int64_t H, int64_t N, int64_t d,
+                               const int64_t *v_strides, const int64_t *o_strides,
+                               aaren_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                               void *hip_stream)
+{
+    if (!scores || !v_strides || !o_strides)
+        return fail(AAREN_ERR_INVALID_ARG, "scores or strides are NULL");
+    return scan_dense(scores, scores, v, o, nullptr, B, H, N, d, v_strides, o_strides, 1.f,
+                      AAREN_F32, out_dtype, workspace, workspace_bytes, hip_stream, nullptr, scores,
+                      s_head_stride, true);
+}
+}  // namespace aaren
 
 // ---- backward of the dense scan -----------------------------------------------
 

@@ -44,6 +44,15 @@ size_t round256(size_t x)
 extern "C" aaren_status aaren_layer_fail(aaren_status s, const char *msg);
 
 namespace aaren {
+// scan_scored_strided's argument checks alone, enqueueing nothing (api.hip)
+aaren_status scan_scored_check(const float *scores, int64_t s_head_stride, const float *v,
+                               void *o, int64_t B, int64_t H, int64_t N, int64_t d,
+                               const int64_t *v_strides, const int64_t *o_strides,
+                               aaren_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                               void *hip_stream);
+}  // namespace aaren
+
+namespace aaren {
 
 // Creates the handle and runs one small product of the layer's types and
 // layout through it, so that rocBLAS has loaded its kernels for them before a
@@ -208,6 +217,16 @@ AAREN_API aaren_status aaren_layer_forward(const void *x, const void *w_kv, cons
     uint16_t *w2 = reinterpret_cast<uint16_t *>(wsb + round256(scan_bytes) +
                                                 round256((size_t)(rows * cols) * 4));
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const int64_t vstr[3] = {N * cols, d, cols};   // V: row (b,n), column block h
+    const int64_t os[3] = {N * H * d, d, H * d};   // o: token-major [B,N,H,d]
+    // the scan's own checks, before anything is enqueued
+    {
+        const aaren_status cs = aaren::scan_scored_check(vs + H * d, 4, vs, o, B, H, N, d, vstr,
+                                                         os, out_dtype, workspace, scan_bytes,
+                                                         hip_stream);
+        if (cs != AAREN_OK)
+            return cs;
+    }
     {
         int device = 0;
         if (hipGetDevice(&device) != hipSuccess)
@@ -244,8 +263,6 @@ AAREN_API aaren_status aaren_layer_forward(const void *x, const void *w_kv, cons
         if (bs != rocblas_status_success)
             return aaren_layer_fail(AAREN_ERR_HIP, rocblas_status_to_string(bs));
     }
-    const int64_t vstr[3] = {N * cols, d, cols};   // V: row (b,n), column block h
-    const int64_t os[3] = {N * H * d, d, H * d};   // o: token-major [B,N,H,d]
     return aaren::scan_scored_strided(vs + H * d, 4, vs, o, B, H, N, d, vstr, os, out_dtype,
                                       workspace, scan_bytes, hip_stream);
 }
