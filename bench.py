@@ -590,9 +590,13 @@ def make(name: str, device):
                                  2 * d * B * N * H for l in range(L))
         b.units = B * N
         b.bytes_per_launch = 0
+        # the same layers by the definition's count, K = x W_K formed: context only
+        flops_with_k = sum(2 * B * N * (Dm if l == 0 else H * d) * 2 * H * d + 4 * d * B * N * H
+                           for l in range(L))
         b.config = {"workload": f"{L} stacked Aaren layers {b.describe}", "B": B, "N": N,
                     "Dm": Dm, "H": H, "d": d, "layers": L, "in_dtype": "bf16",
-                    "out_dtype": "bf16", "flops_per_step": b.flops_per_launch}
+                    "out_dtype": "bf16", "flops_per_step": b.flops_per_launch,
+                    "flops_per_step_with_k_formed": flops_with_k}
         b.kernel = "layer_fold_kernel + rocBLAS projection GEMMs + scan_kernel (the whole stack)"
         b.dispatches_per_launch = L  # traffic counters are read per layer (fold, GEMM, scan)
 
