@@ -163,13 +163,37 @@ int64_t ceil_div(int64_t a, int64_t b)
 
 // Consecutive workgroups per stream (see scan.hip). Measured on MI355X with
 // inputs beyond the Infinity Cache: packed batches fastest at 8 (one per XCD:
-// the heads of a token range are adjacent in memory), dense batches at 2-4.
+// the heads of a token range are adjacent in memory); the dense backward at 4.
 constexpr uint32_t kGroupDense = 4;
 constexpr uint32_t kGroupPacked = 8;
 // Token-major layouts (heads side by side in each row, rows far apart): 8
 // consecutive workgroups per head, measured on the layer's K|V (row stride
 // 8 KB): 71 us against 74-79 us with 1, 2 or 4 and 73 us with 16.
 constexpr uint32_t kGroupInterleaved = 8;
+
+// Dense forward scans choose by how many rounds of resident workgroups the
+// call's tiles make (tiles / resident, resident from the kernel's occupancy):
+// one workgroup per stream up to 3 rounds, 2 up to 6, 4 beyond. With one per
+// stream a tile's predecessor was always dispatched `streams` workgroups
+// earlier and a stream's tickets are drawn one at a time, which short calls
+// feel most; long calls keep neighbouring tiles of a stream on different
+// XCDs. Timed interleaved on MI355X (H = 8, N = 4096, d = 64 fp32; the
+// output is the same bit for bit): B = 4, 8, 16 (0.7, 1.3, 2.7 rounds)
+// 20.9, 42.7, 72.9 us with 1 against 22.5, 44.9, 76.3 us with 4; B = 32 (5.3
+// rounds) 136.0 us with 2 against 137.3 with 4 and 138.6 with 1; B = 128 (21
+// rounds) 513.6 us with 4 against 519.5 with 2 and 525.9 with 1. d = 128 bf16:
+// 1 x 8 x 16384 (1 round) 27.5 us with 1 against 31.2 with 4; 4 x 16 x 65536
+// (32 rounds) 686 us with 4 against 702 with 2.
+uint32_t dense_group(int64_t tiles, int resident)
+{
+    if (resident <= 0)
+        return kGroupDense;
+    if (tiles <= 3 * (int64_t)resident)
+        return 1;
+    if (tiles <= 6 * (int64_t)resident)
+        return 2;
+    return 4;
+}
 
 // The ticket counters sit right after the header and their number depends on
 // the call's shape; a call's tile slots start where its counters end. Each
@@ -392,9 +416,10 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
     const int rows = aaren::scan_rows_per_tile((int)d, in_dtype);
     const int64_t chunks = ceil_div(N, rows);
     const int64_t tiles = B * H * chunks;
-    const uint32_t group = kvs[1] < kvs[2] ? kGroupInterleaved : kGroupDense;
-    const int64_t chunks_padded = ceil_div(chunks, group) * group;
-    if (B * H * chunks_padded >= 0x7fffffff)
+    const bool interleaved = kvs[1] < kvs[2];
+    // the grid is largest with the largest group a dense call may take
+    const uint32_t max_group = interleaved ? kGroupInterleaved : kGroupDense;
+    if (B * H * (ceil_div(chunks, max_group) * max_group) >= 0x7fffffff)
         return fail(AAREN_ERR_UNSUPPORTED, "%lld tiles exceed the 2^31-1 launch limit",
                     (long long)tiles);
     const size_t need = scan_workspace_bytes(B * H, tiles, 0, d);
@@ -405,6 +430,11 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
         return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
     if (check_only)
         return AAREN_OK;
+    const uint32_t group =
+        interleaved ? kGroupInterleaved
+        : scores    ? kGroupDense
+                    : dense_group(tiles, aaren::scan_resident_tiles((int)d, in_dtype, out_dtype));
+    const int64_t chunks_padded = ceil_div(chunks, group) * group;
 
     aaren::ScanParams p{};
     p.q = q;

@@ -196,6 +196,9 @@ aaren_status scan_scored_strided(const float *scores, int64_t s_head_stride, con
 hipError_t launch_segment_flags(const int64_t *offsets, int64_t num_seqs, int64_t total_tokens,
                                 uint32_t *bitmap, int64_t words, hipStream_t stream);
 int scan_rows_per_tile(int D, aaren_dtype in);
+// Workgroups of the dense scan kernel for (D, in, out) that the current
+// device holds at once; 0 if unknown.
+int scan_resident_tiles(int D, aaren_dtype in, aaren_dtype out);
 hipError_t launch_step(const StepParams &p, int D, aaren_dtype in, aaren_dtype out,
                        hipStream_t stream);
 hipError_t launch_append(const StepParams &p, int D, aaren_dtype in, aaren_dtype out,

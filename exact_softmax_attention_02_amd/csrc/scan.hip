@@ -36,6 +36,7 @@
 //    parts per row and head, and take the place of K's row and the dot
 //    product; the rest is unchanged.
 // Exponentials are base 2: q is pre-multiplied by scale*log2(e).
+#include <atomic>
 #include <type_traits>
 
 #include "lookback.h"
@@ -451,6 +452,43 @@ hipError_t launch_scan(const ScanParams &p, int D, aaren_dtype in, aaren_dtype o
 int scan_rows_per_tile(int D, aaren_dtype in)
 {
     return scan_tile_rows(D, in == AAREN_F32 ? 4 : 2);
+}
+
+// Workgroups of one instantiation of the dense scan that the current device
+// holds at once (resident workgroups per compute unit times compute units),
+// found once per device and kept; 0 if the runtime cannot say.
+template <int D, typename Tin, typename Tout>
+static int resident_one()
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> known[kMaxDev];  // 0: not yet asked
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
+        return 0;
+    const int seen = known[dev].load(std::memory_order_relaxed);
+    if (seen != 0)
+        return seen > 0 ? seen : 0;
+    int n = -1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(scan_kernel<D, Tin, Tout, 16, 4, false, false>),
+            256, 0) == hipSuccess &&
+        cus > 0 && per_cu > 0)
+        n = cus * per_cu;
+    known[dev].store(n, std::memory_order_relaxed);
+    return n > 0 ? n : 0;
+}
+
+int scan_resident_tiles(int D, aaren_dtype in, aaren_dtype out)
+{
+    if (D == 64) {
+        if (in == AAREN_F32)
+            return out == AAREN_F32 ? resident_one<64, float, float>() : resident_one<64, float, bf16>();
+        return out == AAREN_F32 ? resident_one<64, bf16, float>() : resident_one<64, bf16, bf16>();
+    }
+    if (in == AAREN_F32)
+        return out == AAREN_F32 ? resident_one<128, float, float>() : resident_one<128, float, bf16>();
+    return out == AAREN_F32 ? resident_one<128, bf16, float>() : resident_one<128, bf16, bf16>();
 }
 
 hipError_t launch_segment_flags(const int64_t *offsets, int64_t num_seqs, int64_t total_tokens,
