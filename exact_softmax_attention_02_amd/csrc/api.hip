@@ -44,6 +44,15 @@ uint32_t stress_enabled()
     return (e && e[0] && e[0] != '0') ? 1u : 0u;
 }
 
+// AAREN_HALF_TILES: -1 unset (the library chooses), 0 never, 1 always (fp32)
+int half_tiles_override()
+{
+    const char *e = std::getenv("AAREN_HALF_TILES");
+    if (!e || !e[0])
+        return -1;
+    return e[0] != '0' ? 1 : 0;
+}
+
 bool aligned16(const void *p)
 {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
@@ -346,11 +355,25 @@ AAREN_API aaren_status aaren_workspace_status(const void *workspace, size_t work
 
 // ---- dense scan ---------------------------------------------------------------
 
+// dense_scan_chunks: full tiles, then half tiles for the last full tile and the rest
+static_assert([] { int64_t f = -1; return aaren::dense_scan_chunks(4096, 256, &f) == 17 && f == 15; }(),
+              "4096 rows: 15 full tiles and 2 half tiles");
+static_assert([] { int64_t f = -1; return aaren::dense_scan_chunks(1000, 256, &f) == 6 && f == 2; }(),
+              "1000 rows: 2 full tiles, 488 rows in 4 half tiles");
+static_assert([] { int64_t f = -1; return aaren::dense_scan_chunks(300, 256, &f) == 2 && f == 1; }(),
+              "300 rows: 1 full tile (one is not split), 44 rows in a half tile");
+static_assert([] { int64_t f = -1; return aaren::dense_scan_chunks(0, 256, &f) == 0 && f == 0; }(),
+              "no rows, no tiles");
+
 AAREN_API size_t aaren_scan_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d)
 {
     if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128))
         return 0;
-    const int64_t tiles = mul_checked({B, H, ceil_div(N, aaren::scan_tile_rows_min((int)d))});
+    // the most tiles per stream any input dtype makes: the smallest tiles
+    // give the most (dense_scan_chunks does not grow with the tile height)
+    int64_t full = 0;
+    const int64_t per_stream = aaren::dense_scan_chunks(N, aaren::scan_tile_rows_min((int)d), &full);
+    const int64_t tiles = mul_checked({B, H, per_stream});
     if (tiles < 0)
         return 0;
     return scan_workspace_bytes(B * H, tiles, 0, d);
@@ -414,15 +437,20 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
             return fail(AAREN_ERR_INVALID_ARG, "score head stride");
     }
     const int rows = aaren::scan_rows_per_tile((int)d, in_dtype);
-    const int64_t chunks = ceil_div(N, rows);
-    const int64_t tiles = B * H * chunks;
+    // Full tiles only (the layer's scored scan, and calls where halves would
+    // not pay), or each stream ending in half tiles; the checks below take the
+    // larger grid of the two, so they do not depend on the device.
+    int64_t split_full = 0;
+    const int64_t plain_chunks = ceil_div(N, rows);
+    const int64_t split_chunks = aaren::dense_scan_chunks(N, rows, &split_full);
+    const int64_t max_tiles = B * H * split_chunks;
     const bool interleaved = kvs[1] < kvs[2];
     // the grid is largest with the largest group a dense call may take
     const uint32_t max_group = interleaved ? kGroupInterleaved : kGroupDense;
-    if (B * H * (ceil_div(chunks, max_group) * max_group) >= 0x7fffffff)
+    if (B * H * (ceil_div(split_chunks, max_group) * max_group) >= 0x7fffffff)
         return fail(AAREN_ERR_UNSUPPORTED, "%lld tiles exceed the 2^31-1 launch limit",
-                    (long long)tiles);
-    const size_t need = scan_workspace_bytes(B * H, tiles, 0, d);
+                    (long long)max_tiles);
+    const size_t need = scan_workspace_bytes(B * H, max_tiles, 0, d);
     if (!workspace || workspace_bytes < need)
         return fail(AAREN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
                     need);
@@ -430,10 +458,28 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
         return fail(AAREN_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
     if (check_only)
         return AAREN_OK;
-    const uint32_t group =
-        interleaved ? kGroupInterleaved
-        : scores    ? kGroupDense
-                    : dense_group(tiles, aaren::scan_resident_tiles((int)d, in_dtype, out_dtype));
+    // Half tiles shorten the drain at the end of a call, but add up to two
+    // tiles per stream. They are taken for fp32 inputs only (the kernel that
+    // splits waits on early loads when it widens bf16), for calls of more
+    // than one round of resident workgroups (in one round every tile starts
+    // at once and there is no drain to shorten: B = 4 and a single sequence
+    // measured 3-6% slower with halves), and where the call's tiles still
+    // make the same number of rounds (one more round costs more than the
+    // drain saves).
+    const int resident = scores ? 0 : aaren::scan_resident_tiles((int)d, in_dtype, out_dtype);
+    const int64_t plain_tiles = B * H * plain_chunks;
+    const int forced = half_tiles_override();
+    const bool split =
+        in_dtype == AAREN_F32 && !scores &&
+        (forced >= 0 ? forced == 1
+                     : resident > 0 && plain_tiles > resident &&
+                           ceil_div(max_tiles, resident) == ceil_div(plain_tiles, resident));
+    const int64_t chunks = split ? split_chunks : plain_chunks;
+    const int64_t full_chunks = split ? split_full : plain_chunks;
+    const int64_t tiles = B * H * chunks;
+    const uint32_t group = interleaved ? kGroupInterleaved
+                           : scores    ? kGroupDense
+                                       : dense_group(tiles, resident);
     const int64_t chunks_padded = ceil_div(chunks, group) * group;
 
     aaren::ScanParams p{};
@@ -456,6 +502,7 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
     p.o_head_stride = os[1];
     p.o_row_stride = os[2];
     p.chunks = chunks;
+    p.full_chunks = full_chunks;
     p.group = group;
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
@@ -468,8 +515,11 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
     p.counters = reinterpret_cast<uint32_t *>(ws + aaren::kHeaderBytes);
     p.slots = reinterpret_cast<uint64_t *>(ws + aaren::kHeaderBytes + counter_bytes(B * H));
     if (log_enabled())
-        fprintf(stderr, "[aaren] scan B=%lld H=%lld N=%lld d=%lld tiles=%lld rows/tile=%d\n",
-                (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles, rows);
+        fprintf(stderr,
+                "[aaren] scan B=%lld H=%lld N=%lld d=%lld tiles=%lld rows/tile=%d full tiles per "
+                "stream=%lld of %lld resident=%d group=%u\n",
+                (long long)B, (long long)H, (long long)N, (long long)d, (long long)tiles, rows,
+                (long long)full_chunks, (long long)chunks, resident, group);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const bool cap = capturing(st);
     CHECK(prepare_counters(workspace, counter_bytes(B * H), cap, st, own_record));
@@ -887,6 +937,7 @@ aaren_status scan_packed(const void *q, const void *k, const void *v, void *o, f
     p.head_stride = p.o_head_stride = d;
     p.row_stride = p.o_row_stride = H * d;
     p.chunks = chunks;
+    p.full_chunks = chunks;
     p.group = kGroupPacked;
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;

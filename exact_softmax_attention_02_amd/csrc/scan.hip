@@ -13,7 +13,9 @@
 //  * A tile is ROWS consecutive rows of one stream (a (b,h) sequence, or one
 //    head of a packed batch). A lane group of L lanes reads a 16-byte slice
 //    of each of R consecutive rows per lane (see Slice in device.h), so every
-//    wave-wide load or store covers whole cache lines.
+//    wave-wide load or store covers whole cache lines. A dense stream ends in
+//    half tiles (R/2 rows per group; dense_scan_chunks in layout.h), which
+//    shortens the drain at the end of a call.
 //  * Scores: per-lane partial dot products, summed over the group with a DPP
 //    butterfly (no MFMA: the score is a matrix-vector product, bandwidth-bound).
 //  * Pass 1 reduces each group's rows to one state (maximum first, then the
@@ -59,7 +61,7 @@ struct ScanShape {
 
 // SCORED: the scores come precomputed (p.scores, see ScanParams) and K is not
 // read; dense fp32 values only.
-template <int D, typename Tin, typename Tout, int R, int WAVES, bool SEG, bool SCORED>
+template <int D, typename Tin, typename Tout, int R, int WAVES, bool SEG, bool SCORED, bool SPLIT>
 __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
 {
     using S = ScanShape<D, Tin, R, WAVES>;
@@ -110,8 +112,20 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     }
     const int64_t chunk = chunk32, stream = stream32;
     const int64_t tile = chunk * p.streams + stream;          // slot index
-    const int64_t row0 = chunk * ROWS + (int64_t)grp * R;   // first row of this group
-    const int64_t left = p.rows - row0;
+    // SPLIT: a half tile (past full_chunks) covers ROWS/2 rows, the first
+    // half of the groups, R rows each. A separate instantiation, for fp32
+    // inputs only: with bf16 inputs the extra arithmetic moves the compiler to
+    // wait for the first rows' loads before issuing the rest.
+    int64_t row0 = chunk * ROWS + (int64_t)grp * R;  // first row of this group
+    int64_t lim = p.rows;
+    if constexpr (SPLIT) {
+        if (chunk >= p.full_chunks) {
+            const int64_t tile_row0 = p.full_chunks * ROWS + (chunk - p.full_chunks) * (ROWS / 2);
+            row0 = tile_row0 + (int64_t)grp * R;
+            lim = tile_row0 + ROWS / 2 < p.rows ? tile_row0 + ROWS / 2 : p.rows;
+        }
+    }
+    const int64_t left = lim - row0;
     const int nvalid = left <= 0 ? 0 : (left >= R ? R : (int)left);
 
     // ---- issue every load of the group's rows first --------------------------
@@ -413,9 +427,16 @@ static hipError_t launch_one(const ScanParams &p, hipStream_t stream)
     static_assert(ScanShape<D, Tin, R, WAVES>::ROWS == scan_tile_rows(D, sizeof(Tin)),
                   "tile rows disagree with the workspace sizing");
     static_assert(!SCORED || (std::is_same_v<Tin, float> && !SEG), "scored: dense fp32 values");
-    hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, SEG, SCORED>),
-                       dim3((unsigned)(p.streams * p.chunks_padded)),
-                       dim3(64 * WAVES), 0, stream, p);
+    const dim3 grid((unsigned)(p.streams * p.chunks_padded)), block(64 * WAVES);
+    if constexpr (!SEG && !SCORED && std::is_same_v<Tin, float>) {
+        if (p.full_chunks < p.chunks) {  // the stream ends in half tiles (fp32 inputs only)
+            hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, false, false, true>), grid,
+                               block, 0, stream, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, SEG, SCORED, false>), grid, block, 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -471,7 +492,7 @@ static int resident_one()
     int n = -1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(scan_kernel<D, Tin, Tout, 16, 4, false, false>),
+            &per_cu, reinterpret_cast<const void *>(scan_kernel<D, Tin, Tout, 16, 4, false, false, false>),
             256, 0) == hipSuccess &&
         cus > 0 && per_cu > 0)
         n = cus * per_cu;

@@ -57,6 +57,9 @@
  *    AAREN_STRESS=1 (tests only, read at every call) makes the scans and
  *    their gradients pause tiles at random to perturb the order in which
  *    tiles exchange states; results are unchanged, only slower.
+ *    AAREN_HALF_TILES (tests only, read at every dense scan call) overrides
+ *    the library's choice of ending each fp32 stream in half tiles: "1"
+ *    always, "0" never; results move by rounding only.
  *  - HIP graphs: every call but aaren_init may be captured for replay
  *    (aaren_layer_forward once aaren_init has run on the device).
  *    The scans (aaren_scan, aaren_scan_strided, aaren_scan_segmented) and

@@ -48,9 +48,10 @@ def test_version_and_strings():
 
 def test_workspace_sizes():
     # dense d=64: 256-row tiles, two published states of 72 words per tile
-    # header + one 128-byte ticket counter per stream + two states per tile
+    # header + one 128-byte ticket counter per stream + two states per tile,
+    # 17 tiles per stream (15 full tiles of 256 rows, then 2 half tiles)
     assert aaren.aaren_scan_workspace_size(32, 8, 4096, 64) == \
-        256 + 256 * 128 + 32 * 8 * 16 * 2 * 72 * 8
+        256 + 256 * 128 + 32 * 8 * 17 * 2 * 72 * 8
     assert aaren.aaren_scan_workspace_size(1, 1, 0, 64) == 256 + 256
     assert aaren.aaren_scan_workspace_size(1, 1, 10, 63) == 0
     seg = aaren.aaren_scan_segmented_workspace_size(3, 1000, 8, 64)

@@ -33,6 +33,42 @@ def test_scan_small(B, H, N, d, ind, outd):
     assert scan_header_error(ws) == 0
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [383, 384, 385, 511, 512, 513, 640, 700, 767, 768, 769, 1100])
+def test_scan_stream_ends_in_half_tiles(d, N, monkeypatch):
+    """fp32 streams ending in half tiles (the last full tile split in two, the
+    rows after it in halves; forced here, the library takes them for calls of
+    several rounds of resident workgroups): lengths around the full and half
+    tile edges (256 and 128 rows at d=64, 128 and 64 at d=128), values and
+    the log-normaliser against the oracle."""
+    monkeypatch.setenv("AAREN_HALF_TILES", "1")
+    announce(f"scan half tiles N={N} d={d}")
+    B, H = 2, 3
+    scale = workloads.default_scale(d)
+    q, k, v = workloads.dense_inputs(B, H, N, d, seed=300 + N, device=dev())
+    ws = torch.zeros(aaren.aaren_scan_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev())
+    o, lse = aaren.aaren_scan(q, k, v, scale, workspace=ws, return_lse=True)
+    ref, _, ref_lse = oracle.scan(host32(q), host32(k), host32(v), scale, stats=True)
+    check(o, ref, TOL[torch.float32], "scan")
+    check(lse, ref_lse, TOL[torch.float32], "lse")
+    assert scan_header_error(ws) == 0
+
+
+@pytest.mark.parametrize("mode", ["0", "1"])
+def test_scan_many_rounds_with_and_without_half_tiles(mode, monkeypatch):
+    """A call of two rounds of resident workgroups (32 x 8 streams of 1000
+    rows: 1024 tiles, 1536 with halves), both tilings against the oracle."""
+    monkeypatch.setenv("AAREN_HALF_TILES", mode)
+    announce(f"scan 32x8x1000 half tiles {mode}")
+    B, H, N, d = 32, 8, 1000, 64
+    scale = workloads.default_scale(d)
+    q, k, v = workloads.dense_inputs(B, H, N, d, seed=41, device=dev())
+    ws = torch.zeros(aaren.aaren_scan_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev())
+    o = aaren.aaren_scan(q, k, v, scale, workspace=ws)
+    check(o, oracle.scan(host32(q), host32(k), host32(v), scale), TOL[torch.float32], "scan")
+    assert scan_header_error(ws) == 0
+
+
 def test_scan_single_token_is_exact():
     announce("scan single token exact")
     q, k, v = workloads.dense_inputs(4, 8, 1, 64, seed=7, device=dev())

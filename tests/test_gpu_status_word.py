@@ -39,7 +39,7 @@ def _p(t):
 
 def test_out_of_range_ticket_is_reported_and_reset():
     announce("workspace status: a ticket counter set out of range")
-    B, H, N, d = 1, 2, 1024, 64        # 4 tiles per stream, no padding positions
+    B, H, N, d = 1, 2, 1024, 64        # 5 tiles per stream (3 full, 2 half), no padding
     q, k, v = _inputs(B, H, N, d, 62)
     o = torch.empty_like(k)
     need = aaren.aaren_scan_workspace_size(B, H, N, d)
