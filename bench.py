@@ -68,12 +68,12 @@ MAX_SETS = 8
 def n_sets(bytes_per_step: int) -> int:
     return max(1, min(MAX_SETS, -(-ROTATE_BYTES // bytes_per_step)))
 KERNEL_SOURCES = {
-    "scan": ["scan.hip", "lookback.h", "device.h", "layout.h"],
+    "scan": ["scan.hip", "scan_tiles.h", "lookback.h", "device.h", "layout.h"],
     "backward": ["scan_backward.hip", "lookback.h", "device.h", "layout.h"],
     "step": ["step.hip", "device.h", "layout.h"],
     "append": ["step.hip", "device.h", "layout.h"],
     "self_attention": ["self_attention.hip", "self_attention.h", "device.h", "layout.h"],
-    "layer": ["layer.hip", "scan.hip", "lookback.h", "device.h", "layout.h"],
+    "layer": ["layer.hip", "scan.hip", "scan_tiles.h", "lookback.h", "device.h", "layout.h"],
     "reduce": ["reduce.hip", "device.h", "layout.h"],
     "mean_query": ["reduce.hip", "device.h", "layout.h"],
 }

@@ -10,6 +10,7 @@
 #include <unordered_map>
 
 #include "layout.h"
+#include "scan_tiles.h"
 #include "self_attention.h"
 
 #define AAREN_API extern "C" __attribute__((visibility("default")))
@@ -502,7 +503,6 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
     p.o_head_stride = os[1];
     p.o_row_stride = os[2];
     p.chunks = chunks;
-    p.full_chunks = full_chunks;
     p.group = group;
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;
@@ -524,6 +524,9 @@ aaren_status scan_dense(const void *q, const void *k, const void *v, void *o, fl
     const bool cap = capturing(st);
     CHECK(prepare_counters(workspace, counter_bytes(B * H), cap, st, own_record));
     CHECK(call_epoch(p.header, cap, st, &p.epoch));
+    if (full_chunks < chunks)  // the streams end in half tiles (fp32 inputs)
+        return hip_status(aaren::launch_scan_split(p, full_chunks, (int)d, out_dtype, st),
+                          "scan launch");
     return hip_status(aaren::launch_scan(p, (int)d, in_dtype, out_dtype, false, st),
                       "scan launch");
 }
@@ -937,7 +940,6 @@ aaren_status scan_packed(const void *q, const void *k, const void *v, void *o, f
     p.head_stride = p.o_head_stride = d;
     p.row_stride = p.o_row_stride = H * d;
     p.chunks = chunks;
-    p.full_chunks = chunks;
     p.group = kGroupPacked;
     p.chunks_padded = (uint32_t)chunks_padded;
     p.num_tiles = (uint32_t)tiles;

@@ -70,21 +70,6 @@ __host__ __device__ constexpr int scan_tile_rows_min(int D)
                                                        : scan_tile_rows(D, 2);
 }
 
-// A dense stream of n rows in tiles of `rows`: the last full tile is split in
-// two half tiles, and the rows after the full tiles go in half tiles, so the
-// tiles that end a call move half the bytes and finish sooner. Returns the
-// stream's tile count and sets *full to the number of full tiles. At most
-// two tiles more than ceil(n / rows).
-__host__ __device__ constexpr int64_t dense_scan_chunks(int64_t n, int64_t rows, int64_t *full)
-{
-    const int64_t whole = n / rows;
-    const int64_t f = whole >= 2 ? whole - 1 : whole;
-    const int64_t rest = n - f * rows;
-    const int64_t half = rows / 2;
-    *full = f;
-    return f + rest / half + (rest % half != 0);
-}
-
 struct ScanParams {
     const void *q;
     const void *k;
@@ -108,10 +93,6 @@ struct ScanParams {
     const float *scores;
     int64_t s_head_stride;
     int64_t chunks;          // tiles per stream
-    // Tiles 0 .. full_chunks-1 of a stream cover ROWS rows each, the rest
-    // ROWS/2 each, from row full_chunks * ROWS on (full_chunks = chunks:
-    // every tile full)
-    int64_t full_chunks;
     uint32_t group;          // consecutive workgroups that serve one stream
     uint32_t chunks_padded;  // chunks rounded up to a multiple of group
     uint32_t num_tiles;      // streams * chunks (real tiles)
@@ -215,9 +196,6 @@ aaren_status scan_scored_strided(const float *scores, int64_t s_head_stride, con
 hipError_t launch_segment_flags(const int64_t *offsets, int64_t num_seqs, int64_t total_tokens,
                                 uint32_t *bitmap, int64_t words, hipStream_t stream);
 int scan_rows_per_tile(int D, aaren_dtype in);
-// Workgroups of the dense scan kernel for (D, in, out) that the current
-// device holds at once; 0 if unknown.
-int scan_resident_tiles(int D, aaren_dtype in, aaren_dtype out);
 hipError_t launch_step(const StepParams &p, int D, aaren_dtype in, aaren_dtype out,
                        hipStream_t stream);
 hipError_t launch_append(const StepParams &p, int D, aaren_dtype in, aaren_dtype out,

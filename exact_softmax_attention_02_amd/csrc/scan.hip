@@ -14,7 +14,7 @@
 //    head of a packed batch). A lane group of L lanes reads a 16-byte slice
 //    of each of R consecutive rows per lane (see Slice in device.h), so every
 //    wave-wide load or store covers whole cache lines. A dense stream ends in
-//    half tiles (R/2 rows per group; dense_scan_chunks in layout.h), which
+//    half tiles (R/2 rows per group; dense_scan_chunks in scan_tiles.h), which
 //    shortens the drain at the end of a call.
 //  * Scores: per-lane partial dot products, summed over the group with a DPP
 //    butterfly (no MFMA: the score is a matrix-vector product, bandwidth-bound).
@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "lookback.h"
+#include "scan_tiles.h"
 
 namespace aaren {
 
@@ -61,8 +62,10 @@ struct ScanShape {
 
 // SCORED: the scores come precomputed (p.scores, see ScanParams) and K is not
 // read; dense fp32 values only.
+// SPLIT: tiles full_chunks .. p.chunks-1 of a stream are half tiles (dense
+// fp32 only); other instantiations ignore full_chunks.
 template <int D, typename Tin, typename Tout, int R, int WAVES, bool SEG, bool SCORED, bool SPLIT>
-__global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
+__global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p, const int64_t full_chunks)
 {
     using S = ScanShape<D, Tin, R, WAVES>;
     using SL = Slice<D, Tin>;
@@ -119,8 +122,8 @@ __global__ __launch_bounds__(64 * WAVES) void scan_kernel(const ScanParams p)
     int64_t row0 = chunk * ROWS + (int64_t)grp * R;  // first row of this group
     int64_t lim = p.rows;
     if constexpr (SPLIT) {
-        if (chunk >= p.full_chunks) {
-            const int64_t tile_row0 = p.full_chunks * ROWS + (chunk - p.full_chunks) * (ROWS / 2);
+        if (chunk >= full_chunks) {
+            const int64_t tile_row0 = full_chunks * ROWS + (chunk - full_chunks) * (ROWS / 2);
             row0 = tile_row0 + (int64_t)grp * R;
             lim = tile_row0 + ROWS / 2 < p.rows ? tile_row0 + ROWS / 2 : p.rows;
         }
@@ -420,23 +423,18 @@ __global__ __launch_bounds__(256) void segment_flags_kernel(const int64_t *offse
     bitmap[i] = bits;
 }
 
-template <int D, typename Tin, typename Tout, bool SEG, bool SCORED = false>
-static hipError_t launch_one(const ScanParams &p, hipStream_t stream)
+template <int D, typename Tin, typename Tout, bool SEG, bool SCORED = false, bool SPLIT = false>
+static hipError_t launch_one(const ScanParams &p, hipStream_t stream, int64_t full_chunks = 0)
 {
     constexpr int R = 16, WAVES = 4;
     static_assert(ScanShape<D, Tin, R, WAVES>::ROWS == scan_tile_rows(D, sizeof(Tin)),
                   "tile rows disagree with the workspace sizing");
     static_assert(!SCORED || (std::is_same_v<Tin, float> && !SEG), "scored: dense fp32 values");
-    const dim3 grid((unsigned)(p.streams * p.chunks_padded)), block(64 * WAVES);
-    if constexpr (!SEG && !SCORED && std::is_same_v<Tin, float>) {
-        if (p.full_chunks < p.chunks) {  // the stream ends in half tiles (fp32 inputs only)
-            hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, false, false, true>), grid,
-                               block, 0, stream, p);
-            return hipGetLastError();
-        }
-    }
-    hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, SEG, SCORED, false>), grid, block, 0,
-                       stream, p);
+    static_assert(!SPLIT || (std::is_same_v<Tin, float> && !SEG && !SCORED),
+                  "half tiles: dense fp32 inputs");
+    hipLaunchKernelGGL((scan_kernel<D, Tin, Tout, R, WAVES, SEG, SCORED, SPLIT>),
+                       dim3((unsigned)(p.streams * p.chunks_padded)), dim3(64 * WAVES), 0, stream, p,
+                       full_chunks);
     return hipGetLastError();
 }
 
@@ -451,6 +449,16 @@ static hipError_t dispatch_dtypes(const ScanParams &p, aaren_dtype in, aaren_dty
     if (in == AAREN_BF16 && out == AAREN_F32)
         return launch_one<D, bf16, float, SEG>(p, stream);
     return launch_one<D, bf16, bf16, SEG>(p, stream);
+}
+
+hipError_t launch_scan_split(const ScanParams &p, int64_t full_chunks, int D, aaren_dtype out,
+                             hipStream_t stream)
+{
+    if (D == 64)
+        return out == AAREN_F32 ? launch_one<64, float, float, false, false, true>(p, stream, full_chunks)
+                                : launch_one<64, float, bf16, false, false, true>(p, stream, full_chunks);
+    return out == AAREN_F32 ? launch_one<128, float, float, false, false, true>(p, stream, full_chunks)
+                            : launch_one<128, float, bf16, false, false, true>(p, stream, full_chunks);
 }
 
 hipError_t launch_scan(const ScanParams &p, int D, aaren_dtype in, aaren_dtype out, bool segmented,
