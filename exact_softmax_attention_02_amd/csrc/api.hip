@@ -194,7 +194,7 @@ constexpr uint32_t kGroupInterleaved = 8;
 // rounds) 513.6 us with 4 against 519.5 with 2 and 525.9 with 1. d = 128 bf16:
 // 1 x 8 x 16384 (1 round) 27.5 us with 1 against 31.2 with 4; 4 x 16 x 65536
 // (32 rounds) 686 us with 4 against 702 with 2.
-uint32_t dense_group(int64_t tiles, int resident)
+constexpr uint32_t dense_group(int64_t tiles, int resident)
 {
     if (resident <= 0)
         return kGroupDense;
@@ -204,6 +204,11 @@ uint32_t dense_group(int64_t tiles, int resident)
         return 2;
     return 4;
 }
+static_assert(dense_group(512, 768) == 1 && dense_group(2048, 768) == 1 &&
+                  dense_group(4352, 768) == 2 && dense_group(16384, 512) == 4 &&
+                  dense_group(100, 0) == kGroupDense,
+              "B = 4 and 16 at d = 64 on 768 resident workgroups: 1; B = 32: 2; the long bf16 "
+              "batch: 4; no occupancy known: the default");
 
 // The ticket counters sit right after the header and their number depends on
 // the call's shape; a call's tile slots start where its counters end. Each
@@ -319,6 +324,12 @@ AAREN_API aaren_status aaren_init(void)
     CHECK(hip_status(hipGetDevice(&device), "hipGetDevice"));
     void *ws = nullptr;
     CHECK(scratch_setup(device, &ws));
+    // the dense scans' resident-workgroup counts, found here once so that
+    // no later call (a captured one included) needs to ask the runtime
+    for (int d : {64, 128})
+        for (aaren_dtype in : {AAREN_F32, AAREN_BF16})
+            for (aaren_dtype out : {AAREN_F32, AAREN_BF16})
+                aaren::scan_resident_tiles(d, in, out);
     if (const char *err = aaren::layer_init(device))
         return fail(AAREN_ERR_HIP, "device %d: %s", device, err);
     return AAREN_OK;

@@ -485,27 +485,27 @@ int scan_rows_per_tile(int D, aaren_dtype in)
 
 // Workgroups of one instantiation of the dense scan that the current device
 // holds at once (resident workgroups per compute unit times compute units),
-// found once per device and kept; 0 if the runtime cannot say.
+// kept per device once found; 0 if the runtime cannot say (then asked again
+// at the next call).
 template <int D, typename Tin, typename Tout>
 static int resident_one()
 {
     constexpr int kMaxDev = 64;
-    static std::atomic<int> known[kMaxDev];  // 0: not yet asked
+    static std::atomic<int> known[kMaxDev];  // 0: not found yet
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
         return 0;
     const int seen = known[dev].load(std::memory_order_relaxed);
-    if (seen != 0)
-        return seen > 0 ? seen : 0;
-    int n = -1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+    if (seen > 0)
+        return seen;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, reinterpret_cast<const void *>(scan_kernel<D, Tin, Tout, 16, 4, false, false, false>),
-            256, 0) == hipSuccess &&
-        cus > 0 && per_cu > 0)
-        n = cus * per_cu;
-    known[dev].store(n, std::memory_order_relaxed);
-    return n > 0 ? n : 0;
+            256, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+        return 0;
+    known[dev].store(cus * per_cu, std::memory_order_relaxed);
+    return cus * per_cu;
 }
 
 int scan_resident_tiles(int D, aaren_dtype in, aaren_dtype out)

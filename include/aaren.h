@@ -112,8 +112,12 @@ const char *aaren_last_error(void);
 /* ---- set-up ------------------------------------------------------------------
  * Prepares the calling thread's current HIP device for the calls that keep
  * state in the library: creates the rocBLAS handle aaren_layer_forward runs
- * its projection with (rocBLAS allocates its workspace then), and sets up the
- * static scan workspace of aaren_scan_noalloc. Call it once per
+ * its projection with (rocBLAS allocates its workspace then), sets up the
+ * static scan workspace of aaren_scan_noalloc, and asks the runtime once how
+ * many workgroups of the dense scan the device holds at once (the scans pick
+ * their tiling from it; without aaren_init the first scan call on the device
+ * asks, and a call that gets no answer takes the default tiling, with the same
+ * results up to rounding). Call it once per
  * device, before the first aaren_layer_forward there, and never while a stream
  * of the process is being captured into a graph (it allocates); further calls
  * on an initialised device do nothing. It is the only call that allocates.
