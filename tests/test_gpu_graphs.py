@@ -136,6 +136,37 @@ def test_dense_scan_in_a_graph():
         assert scan_header_error(ws) == 0
 
 
+@pytest.mark.parametrize("half", ["0", "1"])
+def test_dense_scan_of_two_rounds_in_a_graph(half, monkeypatch):
+    """A call of two rounds of resident workgroups (32 x 8 streams of 1000
+    rows: 1024 full tiles, or 1536 with each stream ending in half tiles),
+    captured with either tiling; replays equal eager calls made with the
+    same tiling."""
+    monkeypatch.setenv("AAREN_HALF_TILES", half)
+    announce(f"graph: dense scan 32x8x1000, half tiles {half}")
+    B, H, N, d = 32, 8, 1000, 64
+    g = torch.Generator(device=dev()).manual_seed(37)
+    q, k, v = (torch.empty(*shape, device=dev()) for shape in ((H, d), (B, H, N, d), (B, H, N, d)))
+    _refill(g, q, k, v)
+    ws = torch.zeros(aaren.aaren_scan_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev())
+    o = torch.empty(B, H, N, d, device=dev())
+    aaren.aaren_scan(q, k, v, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        aaren.aaren_scan(q, k, v, out=o, workspace=ws)
+    for _ in range(REPLAYS):
+        _refill(g, q, k, v)
+        o.zero_()
+        _noise()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = aaren.aaren_scan(q, k, v, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref)
+        assert scan_header_error(ws) == 0
+
+
 def test_graph_replays_between_calls_of_other_shapes():
     """A scan of 256 streams captured into a graph, with eager scans of 8
     streams on the same workspace before every replay: the small calls' tile
