@@ -69,6 +69,21 @@ def test_scan_many_rounds_with_and_without_half_tiles(mode, monkeypatch):
     assert scan_header_error(ws) == 0
 
 
+@pytest.mark.parametrize("d,ind", [(64, "f32"), (128, "bf16"), (128, "f32")])
+@pytest.mark.parametrize("half", ["0", "1"])
+def test_scan_bf16_output_is_the_rounded_fp32_output(d, ind, half, monkeypatch):
+    """The bf16 output is the fp32 output of the same call rounded to nearest
+    even (torch's conversion), bit for bit: the kernels round on the chip."""
+    monkeypatch.setenv("AAREN_HALF_TILES", half)
+    announce(f"scan bf16 output rounding d={d} in={ind} half={half}")
+    B, H, N = 2, 3, 1500
+    q, k, v = workloads.dense_inputs(B, H, N, d, seed=55, device=dev(), dtype=ind)
+    o32 = aaren.aaren_scan(q, k, v, out_dtype=torch.float32)
+    o16 = aaren.aaren_scan(q, k, v, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
 def test_scan_single_token_is_exact():
     announce("scan single token exact")
     q, k, v = workloads.dense_inputs(4, 8, 1, 64, seed=7, device=dev())
